@@ -1,0 +1,201 @@
+/*
+ * paged_attn.h — C ABI of the MI355X (gfx950) paged-attention library.
+ *
+ * Three operations, on one GPU:
+ *   paged_attn_decode     one query token per sequence attends to its cached
+ *                         keys/values, read through a block table;
+ *   paged_attn_prefill    the new tokens of each sequence attend causally to
+ *                         the cached prefix and to each other;
+ *   paged_kv_copy_blocks  copies whole cache blocks between two pools by a
+ *                         src_to_dst mapping.
+ *
+ * Pages the operations follow (cited by title):
+ *   [P-swap] "vLLM中FlashAttention与KVCache交换机制解析"
+ *   [P-wall] "大模型长文本推理基座从 FlashAttention 硬件加速机制到 vLLM 核心
+ *             PagedAttention 显存物理布局深度剖析"
+ *   [P-opt]  "vLLM中FlashAttention与KVCache优化解析"
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers on the current HIP device,
+ *     allocated and owned by the caller.  The library allocates and frees
+ *     nothing and keeps no pointer after a call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work: they return before the GPU finishes, never
+ *     synchronise, and are safe to call from several host threads on
+ *     different streams.  Calls that share a workspace must not overlap.
+ *   - Every call validates its host-side arguments first and returns a
+ *     pa_status_t; nothing is launched unless the result is PA_OK.  Errors
+ *     never abort or throw.  A launch failure reported by HIP is PA_ERR_LAUNCH.
+ *   - Arrays are dense and row-major with the shapes given below (no strides).
+ *   - Device-side contents are not validated (that would need a device read):
+ *     out-of-range block ids are clamped into the pool and context lengths are
+ *     clamped to [0, min(max_context_len, max_blocks_per_seq*block_size)], so
+ *     a bad table gives a meaningless result but never a memory fault.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,         /* a required pointer is NULL                       */
+  PA_ERR_DTYPE = -2,        /* unknown dtype, or a dtype the operation lacks    */
+  PA_ERR_SHAPE = -3,        /* a size is negative/zero where it must not be, or
+                               sizes are inconsistent (e.g. heads % kv_heads)   */
+  PA_ERR_UNSUPPORTED = -4,  /* valid but not built: head_dim, block_size,
+                               partition size, alignment                        */
+  PA_ERR_WORKSPACE = -5,    /* workspace NULL or smaller than the query says    */
+  PA_ERR_LAUNCH = -6,       /* HIP reported an error while enqueueing           */
+  PA_ERR_DEVICE = -7        /* no usable HIP device is current                  */
+} pa_status_t;
+
+typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } pa_dtype_t;
+
+/* Library default KV partition length, in tokens, for split-KV decode. */
+#define PA_DEFAULT_PARTITION 512
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *pa_status_string(pa_status_t status);
+
+/* --------------------------------------------------------------------------
+ * Paged decode.
+ *
+ * Computes, for every sequence b and query head h,
+ *   out[b,h,:] = softmax(scale * q[b,h,:] . K_b^T) V_b
+ * where K_b/V_b are the first context_lens[b] cached rows of kv head
+ * g = h / (num_heads/num_kv_heads), gathered in logical order: row j lives in
+ * physical block block_tables[b, j / block_size], slot j % block_size.
+ * This is scaled dot-product attention (formula at the top of [P-swap]) over
+ * the PagedAttention cache ([P-wall] §二.2; [P-opt] "Block Table 管理"), with
+ * query heads of a GQA group sharing one kv head by indexing, not by copying
+ * ([P-swap], the MQA/GQA remarks).  Long contexts are cut into partitions of
+ * `partition_size` tokens whose partial (M, L, O) states are merged with the
+ * rescaling of the OnlineSoftmax update ([P-swap], M_new/L_new/O_new).
+ *
+ *   out          [num_seqs, num_heads, head_dim]                 dtype, written
+ *   query        [num_seqs, num_heads, head_dim]                 dtype
+ *   k_cache      [num_blocks, num_kv_heads, block_size, head_dim] dtype
+ *   v_cache      [num_blocks, num_kv_heads, block_size, head_dim] dtype
+ *   block_tables [num_seqs, max_blocks_per_seq] int32 physical block ids;
+ *                entries past ceil(context_len/block_size) are never read
+ *   context_lens [num_seqs] int32, keys attended per sequence (the current
+ *                token's own K/V included), 1 <= context_lens[b] <= max_context_len
+ *   max_context_len  host-side upper bound of context_lens (sizes the work)
+ *   scale        softmax scale (normally 1/sqrt(head_dim))
+ *   partition_size  tokens per split-KV partition: 0 = PA_DEFAULT_PARTITION,
+ *                a positive multiple of 64, or -1 = never split
+ *   workspace    device scratch of at least
+ *                paged_attn_decode_workspace_size(...) bytes; contents on entry
+ *                are ignored and are clobbered
+ *
+ * Supported: dtype f32/f16/bf16 (query, caches and out share it; arithmetic
+ * is fp32), head_dim 64 or 128, block_size a power of two in [8, 256],
+ * num_heads % num_kv_heads == 0.  A sequence with context_lens[b] < 1 leaves
+ * out[b] unwritten.
+ * ------------------------------------------------------------------------ */
+size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t max_context_len, int32_t partition_size);
+
+pa_status_t paged_attn_decode(void *out, const void *query, const void *k_cache,
+                              const void *v_cache, const int32_t *block_tables,
+                              const int32_t *context_lens, int32_t num_seqs,
+                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, int32_t max_context_len,
+                              float scale, pa_dtype_t dtype, int32_t partition_size,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* --------------------------------------------------------------------------
+ * Causal paged prefill / append.
+ *
+ * The new tokens of sequence b are rows query_start_loc[b] ..
+ * query_start_loc[b+1]-1 of the packed `query`; with q_b of them and
+ * n = context_lens[b] keys in the cache (prefix + new, all already written),
+ * new token t sits at position n - q_b + t and attends to keys 0..n-q_b+t
+ * (bottom-right causal alignment).  This is the prefill step of the serving
+ * flow in [P-swap] (prefill through FlashAttention over the paged cache),
+ * computed with tiled QK^T and PV and the OnlineSoftmax update, with S and P
+ * never leaving the chip ([P-swap] Kernel Fusion + Tiling + OnlineSoftmax).
+ *
+ *   out, query       [total_query_tokens, num_heads, head_dim] dtype
+ *   k_cache, v_cache [num_blocks, num_kv_heads, block_size, head_dim] dtype
+ *   block_tables     [num_seqs, max_blocks_per_seq] int32
+ *   context_lens     [num_seqs] int32, prefix + new keys
+ *   query_start_loc  [num_seqs + 1] int32, non-decreasing, [0] = 0,
+ *                    [num_seqs] = total_query_tokens, and
+ *                    q_b <= context_lens[b] for every b
+ *   max_query_len    host-side upper bound of q_b
+ *   max_context_len  host-side upper bound of context_lens
+ *
+ * Supported: dtype f16/bf16 (matrix-core arithmetic with fp32 accumulation;
+ * f32 returns PA_ERR_DTYPE), head_dim 64 or 128, block_size a power of two
+ * in [8, 256], num_heads % num_kv_heads == 0.  Needs no workspace.
+ * ------------------------------------------------------------------------ */
+pa_status_t paged_attn_prefill(void *out, const void *query, const void *k_cache,
+                               const void *v_cache, const int32_t *block_tables,
+                               const int32_t *context_lens, const int32_t *query_start_loc,
+                               int32_t num_seqs, int32_t total_query_tokens,
+                               int32_t max_query_len, int32_t max_context_len,
+                               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t num_blocks,
+                               int32_t max_blocks_per_seq, float scale, pa_dtype_t dtype,
+                               void *stream);
+
+/* --------------------------------------------------------------------------
+ * Block copy by mapping.
+ *
+ * src_to_dst[i] = j asks for source block i to be copied into destination
+ * block j ([P-swap], swap_blocks and its mapping argument); -1 (or any value
+ * outside [0, num_dst_blocks)) is ignored.  When several i name the same j,
+ * only the lowest such i is considered, and it is copied only if
+ * i < num_src_blocks.  Destination blocks nobody names keep their bytes.  The
+ * K pool pair and the V pool pair are copied with the same mapping in one
+ * call ([P-opt] "Swap Blocks 机制": K and V swapped separately, same map).
+ * Copies are bytewise (NaN payloads and -0 survive).
+ *
+ *   src_k, src_v  [num_src_blocks, block_bytes] bytes (any element type)
+ *   dst_k, dst_v  [num_dst_blocks, block_bytes] bytes; src_v and dst_v may
+ *                 both be NULL to copy one pool only
+ *   src_to_dst    [num_mappings] int64
+ *   block_bytes   bytes per block, a positive multiple of 16; every pool
+ *                 pointer 16-byte aligned
+ *   workspace     device scratch of at least
+ *                 paged_kv_copy_blocks_workspace_size(num_dst_blocks) bytes
+ *
+ * Source and destination pools must not overlap.  num_mappings may be 0
+ * (nothing is launched) and must be below 2^31.
+ * ------------------------------------------------------------------------ */
+size_t paged_kv_copy_blocks_workspace_size(int64_t num_dst_blocks);
+
+pa_status_t paged_kv_copy_blocks(const void *src_k, const void *src_v, void *dst_k,
+                                 void *dst_v, const int64_t *src_to_dst, int64_t num_mappings,
+                                 int64_t num_src_blocks, int64_t num_dst_blocks,
+                                 int64_t block_bytes, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/* --------------------------------------------------------------------------
+ * Measurement hook.
+ *
+ * With non-NULL events (hipEvent_t passed as void*, created by the caller),
+ * every later call records `start` on its stream just before its main kernel
+ * (decode: the attention kernel; prefill: the attention kernel; copy: the copy
+ * kernel) and `stop` just after it, so the caller can read that kernel's
+ * duration with hipEventElapsedTime.  Pass NULL, NULL to stop recording.  The
+ * setting is process-wide and not synchronised: set it from the thread that
+ * issues the calls being measured.  Returns PA_ERR_NULL if exactly one event
+ * is NULL.
+ * ------------------------------------------------------------------------ */
+pa_status_t pa_set_profile_events(void *start, void *stop);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,235 @@
+"""MI355X (gfx950) paged attention: Python binding of libpagedattn.so.
+
+Argument marshalling only.  Every step of decode, prefill and block copy runs
+in the HIP kernels of the shared library; PyTorch supplies device memory and
+the current stream.  The functions carry the names of the C entry points in
+include/paged_attn.h and raise ``PagedAttnError`` on a non-zero status.  If
+the library has not been built, every call raises: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "PagedAttnError", "library_path", "load_library",
+    "paged_attn_decode", "paged_attn_decode_workspace_size",
+    "paged_attn_prefill",
+    "paged_kv_copy_blocks", "paged_kv_copy_blocks_workspace_size",
+    "DEFAULT_PARTITION",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+DEFAULT_PARTITION = 512
+
+_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+_VP = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_set_profile_events": (ctypes.c_int, [_VP, _VP]),
+    "paged_attn_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
+    "paged_attn_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32,
+                                          _I32, _I32, _I32, _I32, ctypes.c_float, ctypes.c_int,
+                                          _I32, _VP, _SZ, _VP]),
+    "paged_attn_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32,
+                                           _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                           ctypes.c_float, ctypes.c_int, _VP]),
+    "paged_kv_copy_blocks_workspace_size": (_SZ, [_I64]),
+    "paged_kv_copy_blocks": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64,
+                                             _VP, _SZ, _VP]),
+}
+
+_lib = None
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libpagedattn.so")
+
+
+def load_library():
+    """Load (once) and return the ctypes handle; raises if it is not built."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with `python -m paged_kv_cache_248_amd.build` "
+                "(there is no non-HIP fallback)")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load_library().pa_status_string(status).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise PagedAttnError(status, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, dims=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dims, got {t.dim()}")
+
+
+def paged_attn_decode_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int,
+                                     head_dim: int, max_context_len: int,
+                                     partition_size: int = 0) -> int:
+    return int(load_library().paged_attn_decode_workspace_size(
+        num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size))
+
+
+def paged_attn_decode(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, block_tables: torch.Tensor,
+                      context_lens: torch.Tensor, scale: float,
+                      max_context_len: Optional[int] = None, partition_size: int = 0,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out[b,h] = softmax(scale * q[b,h] K_b^T) V_b over the paged cache.
+
+    query/out [B, Hq, D]; k_cache/v_cache [num_blocks, Hkv, block_size, D];
+    block_tables int32 [B, max_blocks]; context_lens int32 [B].
+    ``max_context_len`` (host int) bounds context_lens; None means
+    max_blocks * block_size.  partition_size: 0 = default, -1 = never split.
+    """
+    lib = load_library()
+    _need(query, "query", dims=3)
+    dt = query.dtype
+    if dt not in _DTYPE:
+        raise ValueError(f"unsupported dtype {dt}")
+    _need(out, "out", dt, 3)
+    _need(k_cache, "k_cache", dt, 4)
+    _need(v_cache, "v_cache", dt, 4)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    if v_cache.shape != k_cache.shape or out.shape != query.shape:
+        raise ValueError("k_cache/v_cache or out/query shapes differ")
+    B, Hq, D = query.shape
+    nblk, Hkv, bs, Dk = k_cache.shape
+    if Dk != D or block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("inconsistent shapes")
+    mbps = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = mbps * bs
+    need = paged_attn_decode_workspace_size(B, Hq, Hkv, D, max_context_len, partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=query.device)
+    else:
+        _need(workspace, "workspace", torch.uint8, 1)
+    st = lib.paged_attn_decode(_ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, bs,
+                               nblk, mbps, int(max_context_len), float(scale), _DTYPE[dt],
+                               int(partition_size), _ptr(workspace), workspace.numel(),
+                               _stream(stream))
+    _check(st, "paged_attn_decode")
+    return out
+
+
+def paged_attn_prefill(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor,
+                       v_cache: torch.Tensor, block_tables: torch.Tensor,
+                       context_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                       scale: float, max_query_len: int, max_context_len: int,
+                       stream=None) -> torch.Tensor:
+    """Causal prefill/append of packed new tokens over the paged cache.
+
+    query/out [T, Hq, D]; query_start_loc int32 [B+1]; context_lens int32 [B]
+    counts prefix + new keys (all already in the cache).
+    """
+    lib = load_library()
+    _need(query, "query", dims=3)
+    dt = query.dtype
+    if dt not in _DTYPE:
+        raise ValueError(f"unsupported dtype {dt}")
+    _need(out, "out", dt, 3)
+    _need(k_cache, "k_cache", dt, 4)
+    _need(v_cache, "v_cache", dt, 4)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    _need(query_start_loc, "query_start_loc", torch.int32, 1)
+    T, Hq, D = query.shape
+    nblk, Hkv, bs, Dk = k_cache.shape
+    B = context_lens.shape[0]
+    if (Dk != D or out.shape != query.shape or v_cache.shape != k_cache.shape
+            or block_tables.shape[0] != B or query_start_loc.shape[0] != B + 1):
+        raise ValueError("inconsistent shapes")
+    st = lib.paged_attn_prefill(_ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(block_tables), _ptr(context_lens), _ptr(query_start_loc),
+                                B, T, int(max_query_len), int(max_context_len), Hq, Hkv, D, bs,
+                                nblk, block_tables.shape[1], float(scale), _DTYPE[dt],
+                                _stream(stream))
+    _check(st, "paged_attn_prefill")
+    return out
+
+
+def paged_kv_copy_blocks_workspace_size(num_dst_blocks: int) -> int:
+    return int(load_library().paged_kv_copy_blocks_workspace_size(num_dst_blocks))
+
+
+def paged_kv_copy_blocks(src_k: torch.Tensor, src_v: Optional[torch.Tensor], dst_k: torch.Tensor,
+                         dst_v: Optional[torch.Tensor], src_to_dst: torch.Tensor,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """dst[j] <- src[i] for src_to_dst[i] = j (lowest i per j, valid i only),
+    applied to the K pool pair and, if given, the V pool pair."""
+    lib = load_library()
+    _need(src_k, "src_k")
+    _need(dst_k, "dst_k")
+    _need(src_to_dst, "src_to_dst", torch.int64, 1)
+    if (src_v is None) != (dst_v is None):
+        raise ValueError("src_v and dst_v must both be given or both be None")
+    if src_v is not None:
+        _need(src_v, "src_v")
+        _need(dst_v, "dst_v")
+        if src_v.shape != src_k.shape or dst_v.shape != dst_k.shape:
+            raise ValueError("K and V pools must have matching shapes")
+    if src_k.shape[1:] != dst_k.shape[1:] or src_k.dtype != dst_k.dtype:
+        raise ValueError("source and destination blocks differ in shape or dtype")
+    num_src, num_dst = src_k.shape[0], dst_k.shape[0]
+    block_bytes = src_k[0].numel() * src_k.element_size() if num_src else dst_k[0].numel() * dst_k.element_size()
+    need = paged_kv_copy_blocks_workspace_size(num_dst)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dst_k.device)
+    else:
+        _need(workspace, "workspace", torch.uint8, 1)
+    st = lib.paged_kv_copy_blocks(_ptr(src_k), _ptr(src_v), _ptr(dst_k), _ptr(dst_v),
+                                  _ptr(src_to_dst), src_to_dst.numel(), num_src, num_dst,
+                                  block_bytes, _ptr(workspace), workspace.numel(),
+                                  _stream(stream))
+    _check(st, "paged_kv_copy_blocks")

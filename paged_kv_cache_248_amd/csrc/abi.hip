@@ -1,0 +1,246 @@
+// C ABI entry points: host-side validation, workspace sizing and dispatch to
+// the kernel launchers.  Declarations and the argument contract are in
+// include/paged_attn.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <mutex>
+
+#include "../../include/paged_attn.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (dev < 64) cache[dev] = cus;
+  return cus;
+}
+
+namespace {
+hipEvent_t g_prof_start = nullptr;
+hipEvent_t g_prof_stop = nullptr;
+}  // namespace
+
+void profile_begin(hipStream_t stream) {
+  if (g_prof_start) (void)hipEventRecord(g_prof_start, stream);
+}
+void profile_end(hipStream_t stream) {
+  if (g_prof_stop) (void)hipEventRecord(g_prof_stop, stream);
+}
+
+}  // namespace pa
+
+namespace {
+
+bool pow2_in(int32_t v, int32_t lo, int32_t hi) {
+  return v >= lo && v <= hi && (v & (v - 1)) == 0;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Partition length actually used (multiple of 64 tokens) and partition count.
+bool decode_partition(int32_t ctx_cap, int32_t partition_size, int32_t *part, int32_t *nparts) {
+  int64_t P;
+  if (partition_size == 0) P = PA_DEFAULT_PARTITION;
+  else if (partition_size == -1) P = std::max<int64_t>(64, ((int64_t)ctx_cap + 63) / 64 * 64);
+  else if (partition_size > 0 && partition_size % 64 == 0) P = partition_size;
+  else return false;
+  *part = (int32_t)P;
+  *nparts = (int32_t)std::max<int64_t>(1, ((int64_t)ctx_cap + P - 1) / P);
+  return true;
+}
+
+pa_status_t launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
+
+bool device_ok() {
+  int dev = -1;
+  return hipGetDevice(&dev) == hipSuccess && dev >= 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_set_profile_events(void *start, void *stop) {
+  if ((start == nullptr) != (stop == nullptr)) return PA_ERR_NULL;
+  pa::g_prof_start = static_cast<hipEvent_t>(start);
+  pa::g_prof_stop = static_cast<hipEvent_t>(stop);
+  return PA_OK;
+}
+
+const char *pa_status_string(pa_status_t s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_DTYPE: return "PA_ERR_DTYPE: dtype unknown or not supported by this operation";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: invalid or inconsistent sizes";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: head_dim, block_size, partition or alignment not supported";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: HIP reported an error while enqueueing";
+    case PA_ERR_DEVICE: return "PA_ERR_DEVICE: no usable HIP device";
+  }
+  return "PA_ERR_UNKNOWN";
+}
+
+size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t max_context_len,
+                                        int32_t partition_size) {
+  (void)num_kv_heads;
+  if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+  int32_t part = 0, nparts = 0;
+  if (!decode_partition(std::max(max_context_len, 1), partition_size, &part, &nparts)) return 0;
+  return pa::decode_workspace_layout(num_seqs, num_heads, head_dim, nparts).total;
+}
+
+pa_status_t paged_attn_decode(void *out, const void *query, const void *k_cache,
+                              const void *v_cache, const int32_t *block_tables,
+                              const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, int32_t max_blocks_per_seq,
+                              int32_t max_context_len, float scale, pa_dtype_t dtype,
+                              int32_t partition_size, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
+      num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
+    return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!pow2_in(block_size, 8, 256)) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)num_seqs * num_heads * head_dim > INT32_MAX ||
+      (int64_t)num_seqs * max_blocks_per_seq > INT32_MAX)
+    return PA_ERR_SHAPE;
+  const int32_t ctx_cap =
+      (int32_t)std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * block_size);
+  int32_t part = 0, nparts = 0;
+  if (!decode_partition(std::max(ctx_cap, 1), partition_size, &part, &nparts))
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || ctx_cap == 0) return PA_OK;
+  if (!out || !query || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+  const pa::DecodeWorkspace ws =
+      pa::decode_workspace_layout(num_seqs, num_heads, head_dim, nparts);
+  if (!workspace || workspace_bytes < ws.total) return PA_ERR_WORKSPACE;
+  if (!device_ok()) return PA_ERR_DEVICE;
+  pa::DecodeLaunch a;
+  a.out = out;
+  a.query = query;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.ctx_cap = ctx_cap;
+  a.partition = part;
+  a.max_parts = nparts;
+  a.scale = scale;
+  a.dtype = (pa::DType)dtype;
+  a.workspace = workspace;
+  return launch_status(pa::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+pa_status_t paged_attn_prefill(void *out, const void *query, const void *k_cache,
+                               const void *v_cache, const int32_t *block_tables,
+                               const int32_t *context_lens, const int32_t *query_start_loc,
+                               int32_t num_seqs, int32_t total_query_tokens,
+                               int32_t max_query_len, int32_t max_context_len, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
+                               pa_dtype_t dtype, void *stream) {
+  if (dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || total_query_tokens < 0 || max_query_len < 0 || max_context_len < 0 ||
+      num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || max_query_len > max_context_len)
+    return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!pow2_in(block_size, 8, 256)) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)total_query_tokens * num_heads * head_dim > INT32_MAX ||
+      (int64_t)num_seqs * max_blocks_per_seq > INT32_MAX)
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0 || total_query_tokens == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !query || !k_cache || !v_cache || !block_tables || !context_lens ||
+      !query_start_loc)
+    return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+  if (!device_ok()) return PA_ERR_DEVICE;
+  pa::PrefillLaunch a;
+  a.out = out;
+  a.query = query;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = query_start_loc;
+  a.num_seqs = num_seqs;
+  a.total_query_tokens = total_query_tokens;
+  a.max_query_len = max_query_len;
+  a.ctx_cap =
+      (int32_t)std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * block_size);
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.scale = scale;
+  a.dtype = (pa::DType)dtype;
+  return launch_status(pa::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t paged_kv_copy_blocks_workspace_size(int64_t num_dst_blocks) {
+  if (num_dst_blocks < 0) return 0;
+  return (size_t)std::max<int64_t>(num_dst_blocks, 1) * sizeof(int32_t);
+}
+
+pa_status_t paged_kv_copy_blocks(const void *src_k, const void *src_v, void *dst_k, void *dst_v,
+                                 const int64_t *src_to_dst, int64_t num_mappings,
+                                 int64_t num_src_blocks, int64_t num_dst_blocks,
+                                 int64_t block_bytes, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+  if (num_mappings < 0 || num_mappings >= (int64_t)INT32_MAX || num_src_blocks < 0 ||
+      num_dst_blocks < 0 || block_bytes <= 0)
+    return PA_ERR_SHAPE;
+  if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  const int64_t slices = (block_bytes + 16383) / 16384;
+  if (num_dst_blocks > 0 && slices > (int64_t)INT32_MAX / num_dst_blocks) return PA_ERR_SHAPE;
+  if (num_mappings == 0 || num_dst_blocks == 0 || num_src_blocks == 0) return PA_OK;
+  if (!src_k || !dst_k || !src_to_dst) return PA_ERR_NULL;
+  if ((src_v == nullptr) != (dst_v == nullptr)) return PA_ERR_NULL;
+  if (!aligned16(src_k) || !aligned16(dst_k) || (src_v && (!aligned16(src_v) || !aligned16(dst_v))))
+    return PA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < paged_kv_copy_blocks_workspace_size(num_dst_blocks))
+    return PA_ERR_WORKSPACE;
+  if (!device_ok()) return PA_ERR_DEVICE;
+  pa::CopyLaunch a;
+  a.src_k = src_k;
+  a.src_v = src_v;
+  a.dst_k = dst_k;
+  a.dst_v = dst_v;
+  a.src_to_dst = src_to_dst;
+  a.num_mappings = num_mappings;
+  a.num_src = num_src_blocks;
+  a.num_dst = num_dst_blocks;
+  a.block_bytes = block_bytes;
+  a.first_src = static_cast<int32_t *>(workspace);
+  return launch_status(pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Block copy by mapping for gfx950.
+//
+// src_to_dst[i] = j copies source block i into destination block j, -1 marks
+// an unused entry ("vLLM中FlashAttention与KVCache交换机制解析", swap_blocks
+// signature, argument list and simplified CPU implementation).  For each
+// destination the lowest i naming it is the candidate and is copied only if it
+// is a valid source block.  The same mapping is applied to the K pool and to
+// the V pool ("vLLM中FlashAttention与KVCache优化解析", Swap Blocks 机制).
+//
+// Three short kernels, all on the caller's stream:
+//   1. fill:    first_src[d] = INT32_MAX for every destination block;
+//   2. resolve: first_src[src_to_dst[i]] = min(i) with an atomic min, so the
+//               answer does not depend on execution order;
+//   3. copy:    one work-group per 16 KiB slice of a destination block moves
+//               K and V with 16-byte non-temporal loads and stores (data is
+//               touched once; keeping it out of the caches leaves them to the
+//               attention kernels).
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+constexpr int64_t kSliceBytes = (int64_t)kCopyThreads * 16 * kCopyUnroll;   // 16 KiB
+
+__global__ __launch_bounds__(256) void copy_fill_kernel(int32_t *first_src, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) first_src[i] = 0x7fffffff;
+}
+
+__global__ __launch_bounds__(256) void copy_resolve_kernel(const int64_t *src_to_dst, int64_t nm,
+                                                           int64_t num_dst, int32_t *first_src) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nm) return;
+  const int64_t j = src_to_dst[i];
+  if (j >= 0 && j < num_dst) atomicMin(first_src + j, (int32_t)i);
+}
+
+__device__ __forceinline__ u32x4 ldnt(const u32x4 *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void stnt(u32x4 *p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+
+__global__ __launch_bounds__(256) void copy_kernel(const char *src_k, const char *src_v,
+                                                   char *dst_k, char *dst_v,
+                                                   const int32_t *first_src, int64_t num_src,
+                                                   int64_t block_bytes, int64_t slices) {
+  const int64_t d = blockIdx.x / slices;
+  const int64_t slice = blockIdx.x - d * slices;
+  const int32_t i = first_src[d];
+  if ((int64_t)i >= num_src) return;    // no valid source (INT32_MAX if nobody named d)
+  const int64_t base = slice * kSliceBytes;
+  const size_t so = (size_t)i * block_bytes, dof = (size_t)d * block_bytes;
+  u32x4 kr[kCopyUnroll], vr[kCopyUnroll];
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t off = base + ((int64_t)u * kCopyThreads + threadIdx.x) * 16;
+    if (off < block_bytes) {
+      kr[u] = ldnt(reinterpret_cast<const u32x4 *>(src_k + so + off));
+      if (src_v) vr[u] = ldnt(reinterpret_cast<const u32x4 *>(src_v + so + off));
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t off = base + ((int64_t)u * kCopyThreads + threadIdx.x) * 16;
+    if (off < block_bytes) {
+      stnt(reinterpret_cast<u32x4 *>(dst_k + dof + off), kr[u]);
+      if (src_v) stnt(reinterpret_cast<u32x4 *>(dst_v + dof + off), vr[u]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_copy_blocks(const CopyLaunch &a, hipStream_t stream) {
+  if (a.num_mappings == 0 || a.num_dst == 0) return hipSuccess;
+  const int64_t fill_blocks = (a.num_dst + 255) / 256;
+  hipLaunchKernelGGL(copy_fill_kernel, dim3((unsigned)fill_blocks), dim3(256), 0, stream,
+                     a.first_src, a.num_dst);
+  const int64_t res_blocks = (a.num_mappings + 255) / 256;
+  hipLaunchKernelGGL(copy_resolve_kernel, dim3((unsigned)res_blocks), dim3(256), 0, stream,
+                     a.src_to_dst, a.num_mappings, a.num_dst, a.first_src);
+  const int64_t slices = (a.block_bytes + kSliceBytes - 1) / kSliceBytes;
+  const int64_t grid = slices * a.num_dst;
+  profile_begin(stream);
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)grid), dim3(kCopyThreads), 0, stream,
+                     static_cast<const char *>(a.src_k), static_cast<const char *>(a.src_v),
+                     static_cast<char *>(a.dst_k), static_cast<char *>(a.dst_v), a.first_src,
+                     a.num_src, a.block_bytes, slices);
+  profile_end(stream);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,111 @@
+// Device helpers shared by the gfx950 kernels: element types, conversions,
+// 16-byte vector moves and wavefront (64-lane) reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Storage element tags.  bf16 values are carried as raw 16-bit patterns.
+struct F32 { typedef float storage; static constexpr int bytes = 4; };
+struct F16 { typedef _Float16 storage; static constexpr int bytes = 2; };
+struct BF16 { typedef uint16_t storage; static constexpr int bytes = 2; };
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// fp32 -> bf16, round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  return (uint32_t)f32_to_f16_bits(a) | ((uint32_t)f32_to_f16_bits(b) << 16);
+}
+
+__device__ __forceinline__ u32x4 ld16(const void *p) {
+  return *reinterpret_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+
+// ---- DPP lane exchange inside a row of 16 lanes ---------------------------
+// quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror.  Each step
+// combines a lane with one partner; after the four steps every lane of the
+// row holds the same total (each pairwise sum has the same two operands, so
+// the lanes agree bit for bit).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+  const int lane = __lane_id();
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+      (lane ^ mask) << 2, __builtin_bit_cast(int, v)));
+}
+
+// Sum over aligned groups of N lanes (N = 8, 16, 32, 64); every lane of a
+// group receives the group total.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 8 || N == 16 || N == 32 || N == 64, "group size");
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp<kDppMirror>(v);
+  if constexpr (N >= 32) v += shfl_xor(v, 16);
+  if constexpr (N >= 64) v += shfl_xor(v, 32);
+  return v;
+}
+
+// Max over lanes that differ only in the bits of STRIDE..32 (i.e. combine
+// the 64/STRIDE groups of STRIDE lanes).  STRIDE = 64 is a no-op.
+template <int STRIDE>
+__device__ __forceinline__ float across_groups_max(float v) {
+  if constexpr (STRIDE <= 16) v = fmaxf(v, shfl_xor(v, 16));
+  if constexpr (STRIDE <= 8) v = fmaxf(v, shfl_xor(v, 8));
+  if constexpr (STRIDE <= 32) v = fmaxf(v, shfl_xor(v, 32));
+  return v;
+}
+
+template <int STRIDE>
+__device__ __forceinline__ float across_groups_sum(float v) {
+  // Fixed order so every lane computes the same association.
+  if constexpr (STRIDE <= 8) v += shfl_xor(v, 8);
+  if constexpr (STRIDE <= 16) v += shfl_xor(v, 16);
+  if constexpr (STRIDE <= 32) v += shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pa

@@ -1,0 +1,72 @@
+// Internal launcher interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+struct DecodeLaunch {
+  void *out;
+  const void *query;
+  const void *k_cache;
+  const void *v_cache;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  int32_t num_seqs, num_heads, num_kv_heads, head_dim;
+  int32_t block_size, num_blocks, max_blocks_per_seq;
+  int32_t ctx_cap;      // min(max_context_len, max_blocks_per_seq * block_size)
+  int32_t partition;    // tokens per partition (multiple of 64)
+  int32_t max_parts;    // ceil(ctx_cap / partition)
+  float scale;
+  DType dtype;
+  void *workspace;
+};
+
+// Workspace layout of the decode path, shared by size query and launcher.
+struct DecodeWorkspace {
+  size_t count_off, work_off, part_o_off, part_ml_off, total;
+};
+DecodeWorkspace decode_workspace_layout(int64_t num_seqs, int64_t num_heads, int64_t head_dim,
+                                        int64_t max_parts);
+
+hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream);
+
+struct PrefillLaunch {
+  void *out;
+  const void *query;
+  const void *k_cache;
+  const void *v_cache;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  const int32_t *query_start_loc;
+  int32_t num_seqs, total_query_tokens, max_query_len, ctx_cap;
+  int32_t num_heads, num_kv_heads, head_dim;
+  int32_t block_size, num_blocks, max_blocks_per_seq;
+  float scale;
+  DType dtype;
+};
+
+hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t stream);
+
+struct CopyLaunch {
+  const void *src_k, *src_v;
+  void *dst_k, *dst_v;
+  const int64_t *src_to_dst;
+  int64_t num_mappings, num_src, num_dst, block_bytes;
+  int32_t *first_src;  // workspace, num_dst entries
+};
+
+hipError_t launch_copy_blocks(const CopyLaunch &a, hipStream_t stream);
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+// Records the caller's measurement events (if set) around a main kernel.
+void profile_begin(hipStream_t stream);
+void profile_end(hipStream_t stream);
+
+}  // namespace pa
