@@ -77,18 +77,24 @@ __device__ __forceinline__ float dot16(const u32x4 &q, const u32x4 &k) {
     return fmaf(__uint_as_float(q[3]), __uint_as_float(k[3]), s);
   } else if constexpr (sizeof(typename E::storage) == 2 && E::bytes == 2 &&
                        __is_same(typename E::storage, _Float16)) {
+    // Elements are copied to scalars before the bit cast: a bit cast of an
+    // indexed vector element miscompiles (every index reads element 0).
+    const uint32_t qa[4] = {q.x, q.y, q.z, q.w};
+    const uint32_t ka[4] = {k.x, k.y, k.z, k.w};
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, q[i]),
-                                 __builtin_bit_cast(f16x2, k[i]), s, false);
+      s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qa[i]),
+                                 __builtin_bit_cast(f16x2, ka[i]), s, false);
     return s;
   } else {
+    const uint32_t qa[4] = {q.x, q.y, q.z, q.w};
+    const uint32_t ka[4] = {k.x, k.y, k.z, k.w};
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[i]),
-                                          __builtin_bit_cast(bf16x2, k[i]), s, false);
+      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qa[i]),
+                                          __builtin_bit_cast(bf16x2, ka[i]), s, false);
     return s;
   }
 }

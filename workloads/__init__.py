@@ -27,8 +27,8 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-from .work import (copy_bytes, decode_kv_bytes, kv_cache_bytes, prefill_flops,  # noqa: F401
-                   prefill_pairs)
+from .work import (copy_bytes, copy_count_unique, decode_kv_bytes, kv_cache_bytes,  # noqa: F401
+                   prefill_flops, prefill_pairs)
 
 DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
