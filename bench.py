@@ -220,6 +220,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--only", default=None, choices=["llama7b_decode_f16", "gqa_decode_bf16",
+                                                       "long_decode_f16", "prefill_bf16",
+                                                       "copy_bf16"],
+                    help="run one workload, print its result object and exit (profiling)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
     args = ap.parse_args()
@@ -242,6 +246,18 @@ def main() -> int:
     props = torch.cuda.get_device_properties(0)
     log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), "
         f"{props.multi_processor_count} CUs")
+
+    if args.only:
+        log(f"generating {args.only} ...")
+        case = wl.WORKLOADS[args.only](device=dev)
+        if args.only.startswith("prefill"):
+            r = bench_prefill(pa, torch, wl, case, args.steps, args.warmup)
+        elif args.only.startswith("copy"):
+            r = bench_copy(pa, torch, wl, case, args.steps, args.warmup)
+        else:
+            r = bench_decode(pa, torch, wl, case, args.steps, args.warmup)
+        print(json.dumps(r), flush=True)
+        return 0
 
     log("generating llama7b_decode_f16 ...")
     head = wl.llama7b_decode_f16(device=dev)

@@ -96,11 +96,12 @@ const char *pa_status_string(pa_status_t s) {
 size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                         int32_t head_dim, int32_t max_context_len,
                                         int32_t partition_size) {
-  (void)num_kv_heads;
-  if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_context_len < 0)
+    return 0;
   int32_t part = 0, nparts = 0;
   if (!decode_partition(std::max(max_context_len, 1), partition_size, &part, &nparts)) return 0;
-  return pa::decode_workspace_layout(num_seqs, num_heads, head_dim, nparts).total;
+  return pa::decode_workspace_layout(num_seqs, num_heads, num_kv_heads, head_dim, nparts).total;
 }
 
 pa_status_t paged_attn_decode(void *out, const void *query, const void *k_cache,
@@ -130,7 +131,7 @@ pa_status_t paged_attn_decode(void *out, const void *query, const void *k_cache,
   if (!aligned16(out) || !aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache))
     return PA_ERR_UNSUPPORTED;
   const pa::DecodeWorkspace ws =
-      pa::decode_workspace_layout(num_seqs, num_heads, head_dim, nparts);
+      pa::decode_workspace_layout(num_seqs, num_heads, num_kv_heads, head_dim, nparts);
   if (!workspace || workspace_bytes < ws.total) return PA_ERR_WORKSPACE;
   if (!device_ok()) return PA_ERR_DEVICE;
   pa::DecodeLaunch a;

@@ -19,17 +19,25 @@
 //     FlashAttention advantages table).
 //
 // Design for CDNA4 (HBM-bound path, ~1-4 flop per byte):
-//   * one wavefront = one work item (sequence, kv head, partition, head
-//     chunk).  The grid is persistent: (#CU x resident waves) wavefronts walk
-//     a compact work list built on device, so no wavefront is launched for an
-//     empty partition and all partitions have equal size;
+//   * one work-group of 4 wavefronts = one work item (sequence, kv head,
+//     partition, head chunk); wavefront w takes tiles w, w+4, ... of the
+//     partition and the four partial states are combined in LDS.  The grid is
+//     persistent and items are handed out through an atomic counter from a
+//     compact list built on device (full partitions first, the shorter last
+//     partitions at the end), so the kernel drains evenly whatever the mix of
+//     context lengths;
+//   * a sequence that spans several partitions leaves (M, L, O~) partials that
+//     a short merge kernel combines; the weights of a (sequence, head) are
+//     computed once in LDS and every partial is then read with independent
+//     loads, so the merge costs a few memory latencies, not one per partial;
 //   * a token row (D * elem bytes) is split into 16-byte pieces, one per lane:
 //     each load instruction moves 1 KiB fully coalesced; the lanes of one
 //     token reduce their partial dot products with DPP row exchanges;
-//   * the next tile's K and V (16 KiB for fp16/D128) are in flight while the
-//     current tile is consumed; block ids are fetched one tile further ahead
-//     through the scalar cache so the dependent id -> data load chain never
-//     stalls the vector pipe;
+//   * the next tile's K and V are in flight while the current tile is
+//     consumed; block ids, work items and context lengths are read through the
+//     constant address space, i.e. with scalar loads whose counter is separate
+//     from the vector loads, and the ids run one tile further ahead, so the
+//     id -> data dependency never drains the K/V pipeline;
 //   * reductions only depend on a token's logical position, never on its
 //     physical block, so permuting the pool leaves results bit-identical.
 #include "pa_device.h"
@@ -39,12 +47,15 @@ namespace pa {
 
 namespace {
 
-template <class E, int D>
+template <class E, int D, int GT>
 struct Geom {
   static constexpr int kRowBytes = D * E::bytes;   // one token row of K or V
   static constexpr int kLPT = kRowBytes / 16;      // lanes per token
   static constexpr int kTPL = 64 / kLPT;           // tokens per load instruction
-  static constexpr int kNL = 8;                    // load instructions per tile per tensor
+  // load instructions per tile per tensor: two tiles of K and V are held in
+  // registers; with 4+ heads per wave the tile is halved to stay within 256
+  // VGPRs (2 waves per SIMD)
+  static constexpr int kNL = GT >= 8 ? 2 : GT >= 4 ? 4 : 8;
   static constexpr int kTile = kNL * kTPL;         // tokens per tile
   static constexpr int kEPL = 16 / E::bytes;       // elements per lane per load
   static_assert(kLPT >= 8 && kLPT <= 32, "row must span 8..32 lanes");
@@ -59,6 +70,7 @@ struct DecodeParams {
   const int32_t *context_lens;
   const int32_t *work;        // (seq, partition) pairs
   const int32_t *work_count;  // number of pairs
+  int32_t *next_item;         // dynamic work counter (zeroed by the plan kernel)
   float *part_o;              // [B, Hq, max_parts, D] unnormalised O
   float *part_ml;             // [B, Hq, max_parts, 2] (M in log2 units, L)
   int32_t num_heads, num_kv_heads, group, head_chunks;
@@ -138,15 +150,39 @@ __device__ __forceinline__ u32x4 pack16(const float *f) {
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Read-only int32 data addressed with wave-uniform indices: through the
+// constant address space the compiler emits scalar loads.
+typedef const __attribute__((address_space(4))) int32_t cint32;
+__device__ __forceinline__ cint32 *as_const(const int32_t *p) {
+  return (cint32 *)(p);
+}
 __device__ __forceinline__ float uniformf(float v) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
 }
 
+
+template <class E>
+__device__ __forceinline__ void store_elem(void *out, size_t idx, float v) {
+  if constexpr (E::bytes == 4) static_cast<float *>(out)[idx] = v;
+  else if constexpr (__is_same(typename E::storage, _Float16))
+    static_cast<uint16_t *>(out)[idx] = f32_to_f16_bits(v);
+  else static_cast<uint16_t *>(out)[idx] = f32_to_bf16(v);
+}
+
+constexpr int kWaves = 4;
+
 template <class E, int D, int GT>
-__global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
-  using G = Geom<E, D>;
+__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
+  using G = Geom<E, D, GT>;
   constexpr int NL = G::kNL, TPL = G::kTPL, LPT = G::kLPT, EPL = G::kEPL, TILE = G::kTile;
-  const int lane = threadIdx.x;
+  __shared__ int s_item;
+  __shared__ float s_m[kWaves][GT], s_l[kWaves][GT];
+  __shared__ __attribute__((aligned(16))) float s_o[kWaves][GT][D];
+
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid >> 6);   // wave-uniform: keeps tile/page math scalar
+  const int lane = tid & 63;
   const int tok = lane / LPT;     // token of each load this lane holds
   const int chunk = lane % LPT;   // 16-byte piece of the row this lane holds
   const int bs = 1 << p.bs_log2;
@@ -155,23 +191,27 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   const char *vbase = static_cast<const char *>(p.v_cache);
   const size_t head_stride = (size_t)bs * G::kRowBytes;          // one (block, head) page
   const size_t block_stride = head_stride * (size_t)Hkv;
-  const int total = uniform(*p.work_count) * Hkv * p.head_chunks;
+  const int total = as_const(p.work_count)[0] * Hkv * p.head_chunks;
 
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+  for (;;) {
+    if (tid == 0) s_item = atomicAdd(p.next_item, 1);
+    __syncthreads();
+    const int item = s_item;
+    if (item >= total) break;
     const int hc = item % p.head_chunks;
     const int rest = item / p.head_chunks;
     const int g = rest % Hkv;
     const int wi = rest / Hkv;
-    const int b = uniform(p.work[2 * wi]);
-    const int part = uniform(p.work[2 * wi + 1]);
-    const int ctx = min(max(uniform(p.context_lens[b]), 0), p.ctx_cap);
+    const int b = as_const(p.work)[2 * wi];
+    const int part = as_const(p.work)[2 * wi + 1];
+    const int ctx = min(max(as_const(p.context_lens)[b], 0), p.ctx_cap);
     const int start = part * p.partition;
     const int end = min(start + p.partition, ctx);
     const int nparts = (ctx + p.partition - 1) / p.partition;
     const int h0 = g * p.group + hc * GT;
     const int nh = min(GT, p.group - hc * GT);
     const int npages = (ctx + bs - 1) >> p.bs_log2;
-    const int32_t *tbl = p.block_tables + (size_t)b * p.max_blocks_per_seq;
+    cint32 *tbl = as_const(p.block_tables) + (size_t)b * p.max_blocks_per_seq;
     const char *kpage_base = kbase + (size_t)g * head_stride + (size_t)chunk * 16;
     const char *vpage_base = vbase + (size_t)g * head_stride + (size_t)chunk * 16;
 
@@ -197,21 +237,24 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
       for (int e = 0; e < EPL; ++e) o[j][e] = 0.f;
     }
 
-    const int ntiles = (end - start + TILE - 1) / TILE;
+    // This wavefront's tiles: wave, wave + 4, ... of the partition.
+    const int ntiles_all = (end - start + TILE - 1) / TILE;
+    const int ntiles = ntiles_all > wave ? (ntiles_all - wave + kWaves - 1) / kWaves : 0;
+    auto tile_start = [&](int t) { return start + (wave + t * kWaves) * TILE; };
 
     // Block ids of the pages each load of a tile touches (wave-uniform).
-    auto fetch_ids = [&](int tile, int *ids) {
-      const int ts = start + tile * TILE;
+    auto fetch_ids = [&](int t, int *ids) {
+      const int ts = tile_start(t);
 #pragma unroll
       for (int L = 0; L < NL; ++L) {
         const int page = (ts + L * TPL) >> p.bs_log2;
         int id = 0;
-        if (tile < ntiles && page < npages) id = tbl[page];
+        if (t < ntiles && page < npages) id = tbl[page];
         ids[L] = (int)min((unsigned)id, (unsigned)(p.num_blocks - 1));
       }
     };
-    auto issue = [&](int tile, const int *ids, u32x4 *kr, u32x4 *vr) {
-      const int ts = start + tile * TILE;
+    auto issue = [&](int t, const int *ids, u32x4 *kr, u32x4 *vr) {
+      const int ts = tile_start(t);
 #pragma unroll
       for (int L = 0; L < NL; ++L) {
         const int page = (ts + L * TPL) >> p.bs_log2;
@@ -226,8 +269,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
         }
       }
     };
-    auto consume = [&](int tile, const u32x4 *kr, const u32x4 *vr) {
-      const int ts = start + tile * TILE;
+    auto consume = [&](int t, const u32x4 *kr, const u32x4 *vr) {
+      const int ts = tile_start(t);
       float x[GT][NL];
 #pragma unroll
       for (int L = 0; L < NL; ++L) {
@@ -273,142 +316,207 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
       }
     };
 
-    int ids_a[NL], ids_b[NL];
-    u32x4 ka[NL], va[NL], kb[NL], vb[NL];
-    fetch_ids(0, ids_a);
-    issue(0, ids_a, ka, va);
-    fetch_ids(1, ids_b);
-    for (int t = 0; t < ntiles; t += 2) {
-      if (t + 1 < ntiles) {
-        issue(t + 1, ids_b, kb, vb);
-        fetch_ids(t + 2, ids_a);
-      }
-      consume(t, ka, va);
-      if (t + 1 < ntiles) {
-        if (t + 2 < ntiles) {
-          issue(t + 2, ids_a, ka, va);
-          fetch_ids(t + 3, ids_b);
+    if (ntiles > 0) {
+      int ids_a[NL], ids_b[NL];
+      u32x4 ka[NL], va[NL], kb[NL], vb[NL];
+      fetch_ids(0, ids_a);
+      issue(0, ids_a, ka, va);
+      fetch_ids(1, ids_b);
+      for (int t = 0; t < ntiles; t += 2) {
+        if (t + 1 < ntiles) {
+          issue(t + 1, ids_b, kb, vb);
+          fetch_ids(t + 2, ids_a);
         }
-        consume(t + 1, kb, vb);
+        consume(t, ka, va);
+        if (t + 1 < ntiles) {
+          if (t + 2 < ntiles) {
+            issue(t + 2, ids_a, ka, va);
+            fetch_ids(t + 3, ids_b);
+          }
+          consume(t + 1, kb, vb);
+        }
       }
     }
 
-    // Combine the lane groups (different tokens, same dims).
+    // Combine the lane groups (different tokens, same dims), then the waves.
 #pragma unroll
     for (int j = 0; j < GT; ++j) {
       l[j] = across_groups_sum<LPT>(l[j]);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[j][e] = across_groups_sum<LPT>(o[j][e]);
     }
-
-    if (tok == 0 && end > start) {
-      if (nparts <= 1) {
+    if (tok == 0) {
 #pragma unroll
-        for (int j = 0; j < GT; ++j) {
-          if (j < nh) {
-            const float inv = 1.0f / l[j];
-            float r[EPL];
+      for (int j = 0; j < GT; ++j) {
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) r[e] = o[j][e] * inv;
-            char *op = static_cast<char *>(p.out) +
-                       ((size_t)(b * Hq + h0 + j) * D) * E::bytes + (size_t)chunk * 16;
-            st16(op, pack16<E>(r));
-          }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < GT; ++j) {
-          if (j < nh) {
-            const size_t slot = ((size_t)(b * Hq + h0 + j) * p.max_parts + part);
-            float *po = p.part_o + slot * D + chunk * EPL;
-#pragma unroll
-            for (int e = 0; e < EPL; e += 4)
-              *reinterpret_cast<f32x4 *>(po + e) = f32x4{o[j][e], o[j][e + 1], o[j][e + 2], o[j][e + 3]};
-            if (chunk == 0) {
-              p.part_ml[slot * 2] = m[j];
-              p.part_ml[slot * 2 + 1] = l[j];
-            }
-          }
+        for (int e = 0; e < EPL; ++e) s_o[wave][j][chunk * EPL + e] = o[j][e];
+        if (chunk == 0) {
+          s_m[wave][j] = m[j];
+          s_l[wave][j] = l[j];
         }
       }
     }
+    __syncthreads();
+
+    // State of the whole partition, one (head, dim) per thread.
+    for (int idx = tid; idx < GT * D; idx += 256) {
+      const int j = idx / D, d = idx % D;
+      if (j >= nh) continue;
+      float M = s_m[0][j];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][j]);
+      float L = 0.f, O = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float c = fast_exp2(s_m[w][j] - M);     // idle waves: 2^-inf = 0
+        L = fmaf(c, s_l[w][j], L);
+        O = fmaf(c, s_o[w][j][d], O);
+      }
+      const size_t row = (size_t)(b * Hq + h0 + j);
+      if (nparts <= 1) {
+        store_elem<E>(p.out, row * D + d, O / L);
+      } else {
+        const size_t slot = row * p.max_parts + part;
+        p.part_o[slot * D + d] = O;
+        if (d == 0) {
+          p.part_ml[slot * 2] = M;
+          p.part_ml[slot * 2 + 1] = L;
+        }
+      }
+    }
+    __syncthreads();   // LDS and s_item are reused by the next item
   }
 }
 
-// Builds the compact list of (sequence, partition) work items.
+// Builds the compact list of (sequence, partition) work items — full-length
+// partitions first, each sequence's shorter last partition after them — and
+// clears the dynamic work counter.
 __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t *context_lens, int num_seqs,
                                                            int partition, int ctx_cap,
-                                                           int32_t *work, int32_t *work_count) {
-  __shared__ int s[1024];
+                                                           int32_t *work, int32_t *work_count,
+                                                           int32_t *next_item) {
+  __shared__ int s_full[1024], s_tail[1024];
+  __shared__ int s_total_full;
   const int tid = threadIdx.x;
-  int base = 0;
-  for (int c0 = 0; c0 < num_seqs; c0 += 1024) {
-    const int b = c0 + tid;
-    int n = 0;
-    if (b < num_seqs) {
-      const int ctx = min(max(context_lens[b], 0), ctx_cap);
-      n = (ctx + partition - 1) / partition;
-    }
-    s[tid] = n;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int t = tid >= off ? s[tid - off] : 0;
-      __syncthreads();
-      s[tid] += t;
-      __syncthreads();
-    }
-    const int excl = base + s[tid] - n;
-    for (int k = 0; k < n; ++k) {
-      work[2 * (excl + k)] = b;
-      work[2 * (excl + k) + 1] = k;
-    }
-    base += s[1023];
+  // pass 1: number of full partitions over all sequences
+  int full_sum = 0;
+  for (int b = tid; b < num_seqs; b += 1024) {
+    const int ctx = min(max(context_lens[b], 0), ctx_cap);
+    full_sum += ctx / partition;
+  }
+  s_full[tid] = full_sum;
+  __syncthreads();
+  for (int off = 512; off > 0; off >>= 1) {
+    if (tid < off) s_full[tid] += s_full[tid + off];
     __syncthreads();
   }
-  if (tid == 0) *work_count = base;
+  if (tid == 0) s_total_full = s_full[0];
+  __syncthreads();
+  const int total_full = s_total_full;
+  __syncthreads();
+  // pass 2: place items, chunk by chunk of 1024 sequences
+  int base_full = 0, base_tail = 0;
+  for (int c0 = 0; c0 < num_seqs; c0 += 1024) {
+    const int b = c0 + tid;
+    int nf = 0, nt = 0;
+    if (b < num_seqs) {
+      const int ctx = min(max(context_lens[b], 0), ctx_cap);
+      nf = ctx / partition;
+      nt = (ctx % partition) != 0;
+    }
+    s_full[tid] = nf;
+    s_tail[tid] = nt;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int a = tid >= off ? s_full[tid - off] : 0;
+      const int c = tid >= off ? s_tail[tid - off] : 0;
+      __syncthreads();
+      s_full[tid] += a;
+      s_tail[tid] += c;
+      __syncthreads();
+    }
+    const int f0 = base_full + s_full[tid] - nf;
+    for (int k = 0; k < nf; ++k) {
+      work[2 * (f0 + k)] = b;
+      work[2 * (f0 + k) + 1] = k;
+    }
+    if (nt) {
+      const int t0 = total_full + base_tail + s_tail[tid] - 1;
+      work[2 * t0] = b;
+      work[2 * t0 + 1] = nf;
+    }
+    base_full += s_full[1023];
+    base_tail += s_tail[1023];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    *work_count = total_full + base_tail;
+    *next_item = 0;
+  }
 }
 
-// Merges the partition partials of each (sequence, head): M = max M_p,
-// L = sum L_p 2^(M_p - M), O = sum O~_p 2^(M_p - M) / L.
+
+// Merges the partition partials of one (sequence, kv head, head chunk):
+// M = max_p M_p, L = sum_p L_p 2^(M_p - M), O = sum_p O~_p 2^(M_p - M) / L —
+// the OnlineSoftmax rescaling applied across partitions.  The per-partition
+// weights 2^(M_p - M) / L of a head are formed once in LDS by the whole
+// work-group; each (head, dim) sum then issues its partial loads back to back.
 template <class E, int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(void *out, const float *part_o,
+__global__ __launch_bounds__(256) void decode_merge_kernel(void *out, const float *part_o,
                                                           const float *part_ml,
                                                           const int32_t *context_lens,
-                                                          int num_heads, int partition,
+                                                          int num_heads, int group, int gt,
+                                                          int head_chunks, int partition,
                                                           int max_parts, int ctx_cap) {
-  const int h = blockIdx.x, b = blockIdx.y;
+  extern __shared__ float s_w[];                  // [max_parts]
+  __shared__ float s_red[256 / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.y;
+  const int hc = blockIdx.x % head_chunks;
+  const int g = blockIdx.x / head_chunks;
   const int ctx = min(max(context_lens[b], 0), ctx_cap);
   const int nparts = (ctx + partition - 1) / partition;
   if (nparts <= 1) return;
-  const size_t slot0 = (size_t)(b * num_heads + h) * max_parts;
-  const float *ml = part_ml + slot0 * 2;
-  float M = -__builtin_inff();
-  for (int q = 0; q < nparts; ++q) M = fmaxf(M, ml[2 * q]);
-  constexpr int PER = D / 64;
-  float acc[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  float L = 0.f;
-  for (int q = 0; q < nparts; ++q) {
-    const float w = fast_exp2(ml[2 * q] - M);
-    L = fmaf(w, ml[2 * q + 1], L);
-    const float *po = part_o + (slot0 + q) * D;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, po[threadIdx.x + 64 * i], acc[i]);
-  }
-  const float inv = 1.0f / L;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int d = threadIdx.x + 64 * i;
-    const float r = acc[i] * inv;
-    const size_t idx = (size_t)(b * num_heads + h) * D + d;
-    if constexpr (E::bytes == 4) {
-      static_cast<float *>(out)[idx] = r;
-    } else if constexpr (__is_same(typename E::storage, _Float16)) {
-      static_cast<uint16_t *>(out)[idx] = f32_to_f16_bits(r);
-    } else {
-      static_cast<uint16_t *>(out)[idx] = f32_to_bf16(r);
+  const int h0 = g * group + hc * gt;
+  const int nh = min(gt, group - hc * gt);
+  for (int j = 0; j < nh; ++j) {
+    const size_t row = (size_t)b * num_heads + h0 + j;
+    const float *ml = part_ml + row * max_parts * 2;
+    // M = max over partitions
+    float mx = -__builtin_inff();
+    for (int q = tid; q < nparts; q += 256) mx = fmaxf(mx, ml[2 * q]);
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
+    if (lane == 0) s_red[wave] = mx;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    __syncthreads();
+    // L = sum of rescaled normalisers; weights kept in LDS
+    float ls = 0.f;
+    for (int q = tid; q < nparts; q += 256) {
+      const float c = fast_exp2(ml[2 * q] - M);
+      s_w[q] = c;
+      ls = fmaf(c, ml[2 * q + 1], ls);
     }
+    for (int off = 32; off > 0; off >>= 1) ls += shfl_xor(ls, off);
+    if (lane == 0) s_red[wave] = ls;
+    __syncthreads();
+    const float inv = 1.0f / ((s_red[0] + s_red[1]) + (s_red[2] + s_red[3]));
+    for (int d = tid; d < D; d += 256) {
+      const float *po = part_o + row * max_parts * D + d;
+      float acc = 0.f;
+      int q = 0;
+      for (; q + 4 <= nparts; q += 4) {
+        const float o0 = po[(size_t)q * D], o1 = po[(size_t)(q + 1) * D];
+        const float o2 = po[(size_t)(q + 2) * D], o3 = po[(size_t)(q + 3) * D];
+        acc = fmaf(s_w[q], o0, acc);
+        acc = fmaf(s_w[q + 1], o1, acc);
+        acc = fmaf(s_w[q + 2], o2, acc);
+        acc = fmaf(s_w[q + 3], o3, acc);
+      }
+      for (; q < nparts; ++q) acc = fmaf(s_w[q], po[(size_t)q * D], acc);
+      store_elem<E>(out, row * D + d, acc * inv);
+    }
+    __syncthreads();
   }
 }
 
@@ -426,6 +534,7 @@ hipError_t launch_typed(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStr
   p.context_lens = a.context_lens;
   p.work = reinterpret_cast<const int32_t *>(w + ws.work_off);
   p.work_count = reinterpret_cast<const int32_t *>(w + ws.count_off);
+  p.next_item = reinterpret_cast<int32_t *>(w + ws.count_off + 4);
   p.part_o = reinterpret_cast<float *>(w + ws.part_o_off);
   p.part_ml = reinterpret_cast<float *>(w + ws.part_ml_off);
   p.num_heads = a.num_heads;
@@ -444,15 +553,17 @@ hipError_t launch_typed(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStr
 
   hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, a.context_lens,
                      a.num_seqs, a.partition, a.ctx_cap, reinterpret_cast<int32_t *>(w + ws.work_off),
-                     reinterpret_cast<int32_t *>(w + ws.count_off));
+                     reinterpret_cast<int32_t *>(w + ws.count_off), p.next_item);
 
+  // Resident work-groups per CU; items are fetched dynamically, so a grid
+  // larger than what fits only queues (it cannot unbalance the work).
   static int occ_cache[3][2][4] = {};
   const int ti = (int)a.dtype, di = D == 128, gi = GT == 1 ? 0 : GT == 2 ? 1 : GT == 4 ? 2 : 3;
   int occ = occ_cache[ti][di][gi];
   if (occ == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_kernel<E, D, GT>, 64, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_kernel<E, D, GT>, 256, 0) !=
             hipSuccess || occ < 1)
-      occ = 4;
+      occ = 2;
     occ_cache[ti][di][gi] = occ;
   }
   const long long upper =
@@ -460,11 +571,12 @@ hipError_t launch_typed(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStr
   const long long resident = (long long)device_cu_count() * occ;
   const int grid = (int)std::max(1LL, std::min(upper, resident));
   profile_begin(stream);
-  hipLaunchKernelGGL((decode_kernel<E, D, GT>), dim3(grid), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((decode_kernel<E, D, GT>), dim3(grid), dim3(256), 0, stream, p);
   profile_end(stream);
   if (a.max_parts > 1) {
-    hipLaunchKernelGGL((decode_merge_kernel<E, D>), dim3(a.num_heads, a.num_seqs), dim3(64), 0,
-                       stream, a.out, p.part_o, p.part_ml, a.context_lens, a.num_heads,
+    hipLaunchKernelGGL((decode_merge_kernel<E, D>), dim3(a.num_kv_heads * p.head_chunks, a.num_seqs),
+                       dim3(256), (size_t)a.max_parts * sizeof(float), stream, a.out, p.part_o,
+                       p.part_ml, a.context_lens, a.num_heads, p.group, GT, p.head_chunks,
                        a.partition, a.max_parts, a.ctx_cap);
   }
   return hipGetLastError();
@@ -487,8 +599,10 @@ hipError_t launch_dim(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStrea
 
 }  // namespace
 
-DecodeWorkspace decode_workspace_layout(int64_t num_seqs, int64_t num_heads, int64_t head_dim,
-                                        int64_t max_parts) {
+DecodeWorkspace decode_workspace_layout(int64_t num_seqs, int64_t num_heads, int64_t num_kv_heads,
+                                        int64_t head_dim, int64_t max_parts) {
+  // counts (work_count, next_item) | work list | partials
+  (void)num_kv_heads;
   DecodeWorkspace w;
   w.count_off = 0;
   w.work_off = 256;
@@ -505,8 +619,8 @@ DecodeWorkspace decode_workspace_layout(int64_t num_seqs, int64_t num_heads, int
 }
 
 hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream) {
-  const DecodeWorkspace ws =
-      decode_workspace_layout(a.num_seqs, a.num_heads, a.head_dim, a.max_parts);
+  const DecodeWorkspace ws = decode_workspace_layout(a.num_seqs, a.num_heads, a.num_kv_heads,
+                                                     a.head_dim, a.max_parts);
   switch (a.dtype) {
     case DType::F32: return launch_dim<F32>(a, ws, stream);
     case DType::F16: return launch_dim<F16>(a, ws, stream);

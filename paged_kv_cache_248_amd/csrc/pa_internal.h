@@ -30,8 +30,8 @@ struct DecodeLaunch {
 struct DecodeWorkspace {
   size_t count_off, work_off, part_o_off, part_ml_off, total;
 };
-DecodeWorkspace decode_workspace_layout(int64_t num_seqs, int64_t num_heads, int64_t head_dim,
-                                        int64_t max_parts);
+DecodeWorkspace decode_workspace_layout(int64_t num_seqs, int64_t num_heads, int64_t num_kv_heads,
+                                        int64_t head_dim, int64_t max_parts);
 
 hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream);
 
