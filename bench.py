@@ -174,6 +174,28 @@ def bench_copy(pa, torch, wl, case, steps, warmup):
     }
 
 
+def bench_stream_copy(torch, steps, warmup, nbytes: int = 2 << 30):
+    """A plain device-to-device copy of known size: the practical HBM ceiling
+    for a read+write stream, and the reference that scales the FETCH_SIZE /
+    WRITE_SIZE counters to bytes."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    for _ in range(warmup):
+        dst.copy_(src)
+    ts = []
+    for _ in range(steps):
+        s.record()
+        dst.copy_(src)
+        e.record()
+        torch.cuda.synchronize()
+        ts.append(s.elapsed_time(e))
+    ms = float(np.median(ts))
+    return {"workload": "stream_copy", "bytes_read": nbytes, "bytes_written": nbytes,
+            "ms": ms, "GBps": 2 * nbytes / (ms * 1e-3) / 1e9}
+
+
 def cpu_baseline(torch, wl, case, budget_s: float):
     """The fp64 oracle on the host cores, sequence by sequence, until the time
     budget is spent; reported in the metric's unit (KV GB/s)."""
@@ -222,7 +244,7 @@ def main() -> int:
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--only", default=None, choices=["llama7b_decode_f16", "gqa_decode_bf16",
                                                        "long_decode_f16", "prefill_bf16",
-                                                       "copy_bf16"],
+                                                       "copy_bf16", "stream_copy"],
                     help="run one workload, print its result object and exit (profiling)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
@@ -247,6 +269,9 @@ def main() -> int:
     log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), "
         f"{props.multi_processor_count} CUs")
 
+    if args.only == "stream_copy":
+        print(json.dumps(bench_stream_copy(torch, args.steps, args.warmup)), flush=True)
+        return 0
     if args.only:
         log(f"generating {args.only} ...")
         case = wl.WORKLOADS[args.only](device=dev)

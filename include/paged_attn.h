@@ -59,6 +59,9 @@ typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } pa_dtype_
 
 /* Library default KV partition length, in tokens, for split-KV decode. */
 #define PA_DEFAULT_PARTITION 512
+/* Most partitions one decode sequence may be split into
+ * (ceil(min(max_context_len, max_blocks_per_seq*block_size) / partition)). */
+#define PA_MAX_PARTITIONS 2048
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *pa_status_string(pa_status_t status);
@@ -89,7 +92,9 @@ const char *pa_status_string(pa_status_t status);
  *   max_context_len  host-side upper bound of context_lens (sizes the work)
  *   scale        softmax scale (normally 1/sqrt(head_dim))
  *   partition_size  tokens per split-KV partition: 0 = PA_DEFAULT_PARTITION,
- *                a positive multiple of 64, or -1 = never split
+ *                a positive multiple of 64, or -1 = never split; at most
+ *                PA_MAX_PARTITIONS partitions per sequence (else
+ *                PA_ERR_UNSUPPORTED)
  *   workspace    device scratch of at least
  *                paged_attn_decode_workspace_size(...) bytes; contents on entry
  *                are ignored and are clobbered
@@ -136,7 +141,9 @@ pa_status_t paged_attn_decode(void *out, const void *query, const void *k_cache,
  *
  * Supported: dtype f16/bf16 (matrix-core arithmetic with fp32 accumulation;
  * f32 returns PA_ERR_DTYPE), head_dim 64 or 128, block_size a power of two
- * in [8, 256], num_heads % num_kv_heads == 0.  Needs no workspace.
+ * in [8, 256], num_heads % num_kv_heads == 0, scale finite and > 0 (else
+ * PA_ERR_UNSUPPORTED).  The softmax weights P enter the PV product rounded to
+ * the input dtype; the normaliser L sums them in fp32.  Needs no workspace.
  * ------------------------------------------------------------------------ */
 pa_status_t paged_attn_prefill(void *out, const void *query, const void *k_cache,
                                const void *v_cache, const int32_t *block_tables,

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <cmath>
 #include <mutex>
 
 #include "../../include/paged_attn.h"
@@ -126,6 +127,7 @@ pa_status_t paged_attn_decode(void *out, const void *query, const void *k_cache,
   int32_t part = 0, nparts = 0;
   if (!decode_partition(std::max(ctx_cap, 1), partition_size, &part, &nparts))
     return PA_ERR_UNSUPPORTED;
+  if (nparts > PA_MAX_PARTITIONS) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0 || ctx_cap == 0) return PA_OK;
   if (!out || !query || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!aligned16(out) || !aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -166,6 +168,7 @@ pa_status_t paged_attn_prefill(void *out, const void *query, const void *k_cache
                                int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
                                pa_dtype_t dtype, void *stream) {
   if (dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || total_query_tokens < 0 || max_query_len < 0 || max_context_len < 0 ||
       num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || num_blocks <= 0 ||
       max_blocks_per_seq <= 0 || max_query_len > max_context_len)

@@ -458,18 +458,18 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t *contex
 
 // Merges the partition partials of one (sequence, kv head, head chunk):
 // M = max_p M_p, L = sum_p L_p 2^(M_p - M), O = sum_p O~_p 2^(M_p - M) / L —
-// the OnlineSoftmax rescaling applied across partitions.  The per-partition
-// weights 2^(M_p - M) / L of a head are formed once in LDS by the whole
-// work-group; each (head, dim) sum then issues its partial loads back to back.
-template <class E, int D>
+// the OnlineSoftmax rescaling applied across partitions.  Wavefront w forms
+// the weights 2^(M_p - M) / L of heads w, w+4, ... in LDS with wave-level
+// reductions; then every (head, dim) sum reads its partials 16 at a time, so
+// a sequence of many partitions costs a few memory round trips.
+template <class E, int D, int GT>
 __global__ __launch_bounds__(256) void decode_merge_kernel(void *out, const float *part_o,
                                                           const float *part_ml,
                                                           const int32_t *context_lens,
-                                                          int num_heads, int group, int gt,
+                                                          int num_heads, int group,
                                                           int head_chunks, int partition,
                                                           int max_parts, int ctx_cap) {
-  extern __shared__ float s_w[];                  // [max_parts]
-  __shared__ float s_red[256 / 64];
+  extern __shared__ float s_w[];                  // [GT][max_parts]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.y;
   const int hc = blockIdx.x % head_chunks;
@@ -477,46 +477,40 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(void *out, const floa
   const int ctx = min(max(context_lens[b], 0), ctx_cap);
   const int nparts = (ctx + partition - 1) / partition;
   if (nparts <= 1) return;
-  const int h0 = g * group + hc * gt;
-  const int nh = min(gt, group - hc * gt);
-  for (int j = 0; j < nh; ++j) {
-    const size_t row = (size_t)b * num_heads + h0 + j;
-    const float *ml = part_ml + row * max_parts * 2;
-    // M = max over partitions
+  const int h0 = g * group + hc * GT;
+  const int nh = min(GT, group - hc * GT);
+  for (int j = wave; j < nh; j += 4) {
+    const float *ml = part_ml + ((size_t)b * num_heads + h0 + j) * max_parts * 2;
     float mx = -__builtin_inff();
-    for (int q = tid; q < nparts; q += 256) mx = fmaxf(mx, ml[2 * q]);
+    for (int q = lane; q < nparts; q += 64) mx = fmaxf(mx, ml[2 * q]);
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
-    if (lane == 0) s_red[wave] = mx;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    __syncthreads();
-    // L = sum of rescaled normalisers; weights kept in LDS
     float ls = 0.f;
-    for (int q = tid; q < nparts; q += 256) {
-      const float c = fast_exp2(ml[2 * q] - M);
-      s_w[q] = c;
+    for (int q = lane; q < nparts; q += 64) {
+      const float c = fast_exp2(ml[2 * q] - mx);
+      s_w[j * max_parts + q] = c;
       ls = fmaf(c, ml[2 * q + 1], ls);
     }
     for (int off = 32; off > 0; off >>= 1) ls += shfl_xor(ls, off);
-    if (lane == 0) s_red[wave] = ls;
-    __syncthreads();
-    const float inv = 1.0f / ((s_red[0] + s_red[1]) + (s_red[2] + s_red[3]));
-    for (int d = tid; d < D; d += 256) {
-      const float *po = part_o + row * max_parts * D + d;
-      float acc = 0.f;
-      int q = 0;
-      for (; q + 4 <= nparts; q += 4) {
-        const float o0 = po[(size_t)q * D], o1 = po[(size_t)(q + 1) * D];
-        const float o2 = po[(size_t)(q + 2) * D], o3 = po[(size_t)(q + 3) * D];
-        acc = fmaf(s_w[q], o0, acc);
-        acc = fmaf(s_w[q + 1], o1, acc);
-        acc = fmaf(s_w[q + 2], o2, acc);
-        acc = fmaf(s_w[q + 3], o3, acc);
-      }
-      for (; q < nparts; ++q) acc = fmaf(s_w[q], po[(size_t)q * D], acc);
-      store_elem<E>(out, row * D + d, acc * inv);
+    const float inv = 1.0f / ls;
+    for (int q = lane; q < nparts; q += 64) s_w[j * max_parts + q] *= inv;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < nh * D; idx += 256) {
+    const int j = idx / D, d = idx % D;
+    const size_t row = (size_t)b * num_heads + h0 + j;
+    const float *po = part_o + row * max_parts * D + d;
+    const float *w = s_w + j * max_parts;
+    float acc = 0.f;
+    int q = 0;
+    for (; q + 16 <= nparts; q += 16) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = po[(size_t)(q + u) * D];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc = fmaf(w[q + u], v[u], acc);
     }
-    __syncthreads();
+    for (; q < nparts; ++q) acc = fmaf(w[q], po[(size_t)q * D], acc);
+    store_elem<E>(out, row * D + d, acc);
   }
 }
 
@@ -574,9 +568,10 @@ hipError_t launch_typed(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStr
   hipLaunchKernelGGL((decode_kernel<E, D, GT>), dim3(grid), dim3(256), 0, stream, p);
   profile_end(stream);
   if (a.max_parts > 1) {
-    hipLaunchKernelGGL((decode_merge_kernel<E, D>), dim3(a.num_kv_heads * p.head_chunks, a.num_seqs),
-                       dim3(256), (size_t)a.max_parts * sizeof(float), stream, a.out, p.part_o,
-                       p.part_ml, a.context_lens, a.num_heads, p.group, GT, p.head_chunks,
+    hipLaunchKernelGGL((decode_merge_kernel<E, D, GT>),
+                       dim3(a.num_kv_heads * p.head_chunks, a.num_seqs), dim3(256),
+                       (size_t)GT * a.max_parts * sizeof(float), stream, a.out, p.part_o,
+                       p.part_ml, a.context_lens, a.num_heads, p.group, p.head_chunks,
                        a.partition, a.max_parts, a.ctx_cap);
   }
   return hipGetLastError();

@@ -40,11 +40,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Two fp32 values -> packed pair, round to nearest even, one instruction
+// (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
-  return (uint32_t)f32_to_f16_bits(a) | ((uint32_t)f32_to_f16_bits(b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), f16x2));
 }
 
 __device__ __forceinline__ u32x4 ld16(const void *p) {

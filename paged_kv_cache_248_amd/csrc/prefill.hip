@@ -32,6 +32,8 @@
 //   * grid order: (sequence, kv head) fastest, query tiles from the last
 //     (most keys) to the first; the (sequence, kv head) of a work-group fixes
 //     its XCD, so the K/V of one head stays in one L2.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -72,19 +74,18 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   else return pack_bf16(a, b);
 }
 
-template <class E>
-__device__ __forceinline__ float lo16(uint32_t w) {
-  if constexpr (__is_same(typename E::storage, _Float16)) return f16_lo(w);
-  else return bf16_lo(w);
-}
-template <class E>
-__device__ __forceinline__ float hi16(uint32_t w) {
-  if constexpr (__is_same(typename E::storage, _Float16)) return f16_hi(w);
-  else return bf16_hi(w);
-}
+// V^T tile layout.  Row d holds the tile's 64 keys; inside every group of 16
+// keys the key order is k -> (k & 3) | bit3(k) << 2 | bit2(k) << 3, which puts
+// the 8 keys one lane feeds to a PV k-step (keys 4h..4h+3 and 8+4h..8+4h+3
+// for lane half h) in one contiguous 16-byte chunk.  Chunk c of row d is
+// stored at c ^ vt_swz(d); the swizzle depends on d mod 32 only, so the
+// operand reads of every 32-row sub-tile share one set of per-lane offsets,
+// and is conflict-free for those reads.
+__device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) & 7) ^ ((d >> 4) & 1); }
 
-// V^T row swizzle: 8-byte chunk c of row d is stored at c ^ vt_swz(d).
-__device__ __forceinline__ int vt_swz(int d) { return ((d >> 3) & 15) ^ (((d & 7) >> 1) << 2); }
+// Raise the running maximum (and rescale O and L) only when a tile's maximum
+// exceeds it by more than 2^kLazy; weights then stay within [0, 2^kLazy].
+constexpr float kLazy = 8.0f;
 
 template <class E, int D>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
@@ -95,11 +96,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   constexpr int UNITS = (kBN / 4) * KCH;        // (4 keys x 1 chunk) staging units
   constexpr int KS = D / 16;                    // MFMA k-steps over head_dim
   constexpr int DT = D / 32;                    // 32-wide output sub-tiles
+  static_assert(2 * BUF <= 65536, "LDS offsets must fit the 16-bit immediate");
   __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;      // query column owned by this lane
   const int half = lane >> 5;
 
@@ -141,10 +143,35 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
     for (int ks = 0; ks < KS; ++ks) qf[ks] = row_ok ? ld16(qp + ks * 32) : u32x4{0u, 0u, 0u, 0u};
   }
 
+  // Per-lane LDS read offsets (the sub-tile / buffer parts are immediates).
+  int k_rd[KS], v_rd[4];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    k_rd[ks] = col * (D * 2) + (((2 * ks + half) ^ (col & (KCH - 1))) * 16);
+#pragma unroll
+  for (int ks2 = 0; ks2 < 4; ++ks2)
+    v_rd[ks2] = K_BYTES + col * VT_ROW + (((2 * ks2 + half) ^ vt_swz(col)) * 16);
+
   // Staging unit of this thread: keys 4kg..4kg+3 of the tile, 16-byte chunk dc.
   const bool stager = tid < UNITS;
   const int kg = tid / KCH;
   const int dc = tid % KCH;
+  int k_wr[4], v_wr[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * kg + i;
+    k_wr[i] = row * (D * 2) + ((dc ^ (row & (KCH - 1))) * 16);
+  }
+  {
+    // the 4 keys land at 16-byte chunk vchunk, byte offset vsub, of each row
+    const int vchunk = 2 * (kg >> 2) + (kg & 1);
+    const int vsub = 8 * ((kg >> 1) & 1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = dc * 8 + e;
+      v_wr[e] = K_BYTES + d * VT_ROW + ((vchunk ^ vt_swz(d)) * 16) + vsub;
+    }
+  }
   const size_t head_stride = (size_t)bs * D * 2;
   const size_t block_stride = head_stride * p.num_kv_heads;
   const char *kb = static_cast<const char *>(p.k_cache) + (size_t)g * head_stride + dc * 16;
@@ -172,15 +199,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
       }
     }
   };
-  auto commit = [&](int buf) {
+  auto commit = [&](char *buf) {
     if (!stager) return;
-    char *kl = lds + buf * BUF;
-    char *vl = kl + K_BYTES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 4 * kg + i;
-      st16(kl + row * (D * 2) + ((dc ^ (row & (KCH - 1))) * 16), kr[i]);
-    }
+    for (int i = 0; i < 4; ++i) st16(buf + k_wr[i], kr[i]);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t a0 = vr[0][w], a1 = vr[1][w], a2 = vr[2][w], a3 = vr[3][w];
@@ -188,9 +210,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
                           __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
       const u32x2 odd = {__builtin_amdgcn_perm(a1, a0, 0x07060302u),
                          __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
-      const int d0 = dc * 8 + 2 * w;
-      *reinterpret_cast<u32x2 *>(vl + d0 * VT_ROW + ((kg ^ vt_swz(d0)) * 8)) = even;
-      *reinterpret_cast<u32x2 *>(vl + (d0 + 1) * VT_ROW + ((kg ^ vt_swz(d0 + 1)) * 8)) = odd;
+      *reinterpret_cast<u32x2 *>(buf + v_wr[2 * w]) = even;
+      *reinterpret_cast<u32x2 *>(buf + v_wr[2 * w + 1]) = odd;
     }
   };
 
@@ -199,102 +220,95 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   for (int i = 0; i < DT; ++i) o[i] = f32x16{};
   float m = -__builtin_inff();
   float l = 0.f;
+  const float c = p.scale_log2e;
+
+  // One key tile on the matrix cores: S^T = K Q^T, softmax update, O^T += V^T P^T.
+  auto compute = [&](const char *buf, int j) {
+    f32x16 s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x16 acc = mfma32<E>(ld16(buf + k_rd[0] + kt * 32 * D * 2), qf[0], f32x16{});
+#pragma unroll
+      for (int ks = 1; ks < KS; ++ks)
+        acc = mfma32<E>(ld16(buf + k_rd[ks] + kt * 32 * D * 2), qf[ks], acc);
+      s[kt] = acc;
+    }
+    // Causal mask where the tile can reach past this wavefront's first
+    // position: key (tile offset kt*32 + 8*(i/4) + 4*half + i%4) > position.
+    if (j * kBN + kBN - 1 > prefix + t0) {
+      const int lim = pos - (j * kBN + 4 * half);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          s[kt][i] = (kt * 32 + 8 * (i >> 2) + (i & 3)) > lim ? -__builtin_inff() : s[kt][i];
+    }
+    // Row maximum on raw scores (scale > 0); the scale is folded into the
+    // exponent: p = 2^(s*c - m).
+    float rmx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = (kt == 0 ? 2 : 0); i < 16; i += 2) rmx = fmaxf(rmx, fmaxf(s[kt][i], s[kt][i + 1]));
+    rmx = fmaxf(rmx, shfl_xor(rmx, 32));
+    const float cand = rmx * c;
+    if (__any(cand > m + kLazy)) {
+      const float m_new = fmaxf(m, cand);
+      const float alpha = m_new > m ? fast_exp2(m - m_new) : 1.0f;
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < DT; ++i) o[i] *= alpha;
+      m = m_new;
+    }
+    // A row with every key so far masked keeps m = -inf; use 0 as its
+    // reference so its weights come out 0 instead of NaN.
+    const float nm = m == -__builtin_inff() ? 0.f : -m;
+    // P^T fragments: k-step ks2 = 2kt + hh takes accumulator entries 8hh..8hh+7.
+    u32x4 pf[4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float e0 = fast_exp2(fmaf(s[kt][8 * hh + 2 * q], c, nm));
+          const float e1 = fast_exp2(fmaf(s[kt][8 * hh + 2 * q + 1], c, nm));
+          l += e0 + e1;
+          w[q] = pack2<E>(e0, e1);
+        }
+        pf[2 * kt + hh] = w;
+      }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int ks2 = 0; ks2 < 4; ++ks2)
+        o[dt] = mfma32<E>(ld16(buf + v_rd[ks2] + dt * 32 * VT_ROW), pf[ks2], o[dt]);
+  };
 
   int id_next = fetch_id(0);
   stage(0, id_next);
   id_next = fetch_id(1);
   int id_after = fetch_id(2);
-  commit(0);
+  commit(lds);
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int cur = j & 1;
+  // Tile j uses buffer j % 2; the loop is unrolled by two so every LDS
+  // offset is a compile-time immediate.
+  auto step = [&](auto cur_tag, int j) {
+    constexpr int CUR = decltype(cur_tag)::value;
     if (j + 1 < ntiles) {
       stage(j + 1, id_next);
       id_next = id_after;
       id_after = fetch_id(j + 3);
     }
-    if (j < wave_tiles) {
-      const char *kl = lds + cur * BUF;
-      const char *vl = kl + K_BYTES;
-      // S^T = K Q^T for two 32-key sub-tiles.
-      f32x16 s[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        f32x16 acc = f32x16{};
-        const int row = kt * 32 + col;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int c = 2 * ks + half;
-          const u32x4 a = ld16(kl + row * (D * 2) + ((c ^ (row & (KCH - 1))) * 16));
-          acc = mfma32<E>(a, qf[ks], acc);
-        }
-        s[kt] = acc;
-      }
-      // Scale to log2 units and apply the causal mask where the tile can
-      // reach past this wavefront's first position.
-      const int key_base = j * kBN + 4 * half;
-      const bool diag = j * kBN + kBN - 1 > prefix + t0;
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = s[kt][i] * p.scale_log2e;
-          if (diag) {
-            const int key = key_base + kt * 32 + 8 * (i >> 2) + (i & 3);
-            if (key > pos) x = -__builtin_inff();
-          }
-          s[kt][i] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);
-      if (__any(m_new > m)) {
-        const float alpha = m_new > m ? fast_exp2(m - m_new) : 1.0f;
-        l *= alpha;
-#pragma unroll
-        for (int i = 0; i < DT; ++i) o[i] *= alpha;
-      }
-      m = m_new;
-      // A row with every key so far masked keeps m = -inf; use 0 as its
-      // reference so its weights come out 0 instead of NaN.
-      const float mref = m == -__builtin_inff() ? 0.f : m;
-      // P^T fragments: k-step ks2 = 2kt + hh takes accumulator entries 8hh..8hh+7.
-      u32x4 pf[4];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          u32x4 w;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float e0 = fast_exp2(s[kt][8 * hh + 2 * q] - mref);
-            const float e1 = fast_exp2(s[kt][8 * hh + 2 * q + 1] - mref);
-            const uint32_t pk = pack2<E>(e0, e1);
-            l += lo16<E>(pk) + hi16<E>(pk);     // normaliser of the rounded weights
-            w[q] = pk;
-          }
-          pf[2 * kt + hh] = w;
-        }
-      // O^T += V^T P^T.
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = dt * 32 + col;
-        const char *vrow = vl + d * VT_ROW;
-        const int sw = vt_swz(d);
-#pragma unroll
-        for (int ks2 = 0; ks2 < 4; ++ks2) {
-          const int c0 = 4 * ks2 + half;        // keys 16ks2 + 4half .. +3
-          const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + ((c0 ^ sw) * 8));
-          const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + (((c0 + 2) ^ sw) * 8));
-          const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-          o[dt] = mfma32<E>(a, pf[ks2], o[dt]);
-        }
-      }
-    }
-    if (j + 1 < ntiles) commit(cur ^ 1);
+    if (j < wave_tiles) compute(lds + CUR * BUF, j);
+    if (j + 1 < ntiles) commit(lds + (CUR ^ 1) * BUF);
     __syncthreads();
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    step(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < ntiles) step(std::integral_constant<int, 1>{}, j + 1);
   }
 
   if (!row_ok || wave_tiles == 0) return;

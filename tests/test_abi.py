@@ -80,6 +80,7 @@ def _decode(lib, **kw):
     (dict(bs=4), PA_ERR_UNSUPPORTED),
     (dict(part=100), PA_ERR_UNSUPPORTED),
     (dict(part=-2), PA_ERR_UNSUPPORTED),
+    (dict(part=64, maxctx=64 * 2049, mbps=10000), PA_ERR_UNSUPPORTED),   # too many partitions
     (dict(query=None), PA_ERR_NULL),
     (dict(bt=None), PA_ERR_NULL),
     (dict(out=P + 2), PA_ERR_UNSUPPORTED),
@@ -127,6 +128,9 @@ def _prefill(lib, **kw):
     (dict(qsl=None), PA_ERR_NULL),
     (dict(v=None), PA_ERR_NULL),
     (dict(k=P + 8), PA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), PA_ERR_UNSUPPORTED),
+    (dict(scale=-0.125), PA_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), PA_ERR_UNSUPPORTED),
     (dict(T=0), PA_OK),
     (dict(B=0), PA_OK),
 ])
