@@ -33,6 +33,10 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16/fp16 matrix peak
 
 METRIC = "paged decode KV GB/s (% of 8 TB/s HBM peak); prefill TFLOP/s (% MFMA peak)"
 
+# Sources of the decode kernel: the traffic figure is only reported while
+# these match the version the counters were collected on.
+DECODE_SOURCES = ["paged_kv_cache_248_amd/csrc/decode.hip", "paged_kv_cache_248_amd/csrc/pa_device.h"]
+
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
@@ -196,9 +200,10 @@ def bench_stream_copy(torch, steps, warmup, nbytes: int = 2 << 30):
             "ms": ms, "GBps": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
-def cpu_baseline(torch, wl, case, budget_s: float):
+def cpu_baseline(torch, wl, case, budget_s: float, min_s: float = 10.0):
     """The fp64 oracle on the host cores, sequence by sequence, until the time
-    budget is spent; reported in the metric's unit (KV GB/s)."""
+    budget is spent (whole passes are repeated until at least ``min_s``);
+    reported in the metric's unit (KV GB/s)."""
     from oracle import decode_ref
     try:
         from threadpoolctl import threadpool_info
@@ -210,30 +215,56 @@ def cpu_baseline(torch, wl, case, budget_s: float):
     Hkv = kv.k_cache.shape[1]
     ctx_all = kv.context_lens.cpu().numpy()
     bs = kv.block_size
-    done, nbytes, spent = 0, 0, 0.0
-    for b in range(B):
-        n = int(ctx_all[b])
-        nb = (n + bs - 1) // bs
-        ids = kv.block_tables[b, :nb].long()
-        k = kv.k_cache.index_select(0, ids).cpu()
-        v = kv.v_cache.index_select(0, ids).cpu()
-        k = (k.float() if k.dtype == torch.bfloat16 else k).numpy()
-        v = (v.float() if v.dtype == torch.bfloat16 else v).numpy()
-        q = case.query[b:b + 1].cpu()
-        q = (q.float() if q.dtype == torch.bfloat16 else q).numpy()
-        t0 = time.perf_counter()
-        decode_ref(q, k, v, np.arange(nb, dtype=np.int32)[None], np.array([n]), case.scale)
-        spent += time.perf_counter() - t0
-        done += 1
-        nbytes += wl.decode_kv_bytes([n], Hq, Hkv, D, bs, wl.ELEM_BYTES[case.dtype])
+    calls, nbytes, spent, passes = 0, 0, 0.0, 0
+    cache = {}
+    while spent < max(min_s, 1e-9) and passes < 50:
+        for b in range(B):
+            n = int(ctx_all[b])
+            nb = (n + bs - 1) // bs
+            if b not in cache:
+                ids = kv.block_tables[b, :nb].long()
+                k = kv.k_cache.index_select(0, ids).cpu()
+                v = kv.v_cache.index_select(0, ids).cpu()
+                q = case.query[b:b + 1].cpu()
+                cache[b] = tuple((x.float() if x.dtype == torch.bfloat16 else x).numpy()
+                                 for x in (q, k, v))
+            q, k, v = cache[b]
+            t0 = time.perf_counter()
+            decode_ref(q, k, v, np.arange(nb, dtype=np.int32)[None], np.array([n]), case.scale)
+            spent += time.perf_counter() - t0
+            calls += 1
+            nbytes += wl.decode_kv_bytes([n], Hq, Hkv, D, bs, wl.ELEM_BYTES[case.dtype])
+            if spent >= budget_s:
+                break
+        passes += 1
         if spent >= budget_s:
             break
     return {
         "value": nbytes / spent / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-        "sample": f"first {done} of {B} sequences of {case.name} (all {Hq} heads), "
-                  f"{spent:.1f} s of fp64 numpy",
+        "sample": f"{calls} single-sequence oracle calls over the {B} sequences of {case.name} "
+                  f"(all {Hq} heads, {passes} pass(es)), {spent:.1f} s of fp64 numpy",
         "seconds": spent,
     }
+
+
+def hbm_traffic(kernel_files, launches_key: str):
+    """Calibrated HBM bytes per launch from the committed PMC summary, or None
+    when the kernel sources changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    try:
+        text = open(path).read()
+        data = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
+    except Exception:
+        return None
+    h = hashlib.sha256()
+    for f in kernel_files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    entry = data.get(launches_key)
+    if not entry or entry.get("source_sha256") != h.hexdigest():
+        return None
+    return entry.get("bytes_per_launch")
 
 
 def main() -> int:
@@ -246,7 +277,7 @@ def main() -> int:
                                                        "long_decode_f16", "prefill_bf16",
                                                        "copy_bf16", "stream_copy"],
                     help="run one workload, print its result object and exit (profiling)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0,
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -346,7 +377,8 @@ def main() -> int:
         "roofline": {
             "bound": "hbm", "kernel": "decode_kernel",
             "achieved": round(res["kernel_GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(res["kernel_GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(res["kernel_GBps"] / HBM_PEAK_GBS, 4),
+            "traffic": hbm_traffic(DECODE_SOURCES, "decode_kernel/llama7b_decode_f16"),
             "kernel_ms": round(res["kernel_ms"], 5), "bytes_per_launch": res["bytes"],
         },
         "cpu_baseline": cpu,

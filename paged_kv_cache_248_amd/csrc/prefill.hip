@@ -29,9 +29,9 @@
 //     reads and the staging writes bank-conflict free;
 //   * LDS is double buffered: the next tile's global loads are in flight while
 //     the current tile is on the matrix cores; block ids run two tiles ahead;
-//   * grid order: (sequence, kv head) fastest, query tiles from the last
-//     (most keys) to the first; the (sequence, kv head) of a work-group fixes
-//     its XCD, so the K/V of one head stays in one L2.
+//   * grid order is XCD-aware: the ids an XCD receives walk one (sequence,
+//     kv head) pair at a time through all its query tiles (the last, with the
+//     most keys, first), so the tiles sharing K/V run together in one L2.
 #include <type_traits>
 
 #include "pa_device.h"
@@ -44,6 +44,7 @@ namespace {
 constexpr int kBN = 64;        // keys per tile
 constexpr int kRows = 32;      // query rows per wavefront
 constexpr int kWaves = 4;
+constexpr int kXcds = 8;       // XCDs of an MI355X; work-group ids are dealt to them round-robin
 
 struct PrefillParams {
   void *out;
@@ -55,6 +56,7 @@ struct PrefillParams {
   const int32_t *query_start_loc;
   int32_t num_heads, num_kv_heads, group, heads_per_wg, subgroups, pos_per_wg;
   int32_t bs_log2, max_blocks_per_seq, num_blocks, ctx_cap, num_seqs;
+  int32_t num_pairs, num_qtiles;
   float scale_log2e;
 };
 
@@ -105,12 +107,26 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   const int col = lane & 31;      // query column owned by this lane
   const int half = lane >> 5;
 
-  // Work-group coordinates.
-  const int bg = blockIdx.x;                      // (sequence, kv head, head subgroup)
-  const int hs = bg % p.subgroups;
-  const int g = (bg / p.subgroups) % p.num_kv_heads;
-  const int b = bg / (p.subgroups * p.num_kv_heads);
-  const int qt = gridDim.y - 1 - blockIdx.y;      // last query tile first
+  // Work-group coordinates.  Work-group ids are dealt round-robin to the 8
+  // XCDs; id -> (xcd, local) -> (pair, query tile) makes each XCD run all the
+  // query tiles of one (sequence, kv head, head subgroup) pair together, so
+  // they stream the same K/V tiles through that XCD's L2 close in time.
+  int pair, qt;
+  {
+    const int n_qt = p.num_qtiles, n_pairs = p.num_pairs;
+    const int id = blockIdx.x;
+    const int xcd = id % kXcds, local = id / kXcds;
+    const int xcd_pairs = (n_pairs - xcd + kXcds - 1) / kXcds;   // pairs xcd, xcd+8, ...
+    if (local < xcd_pairs * n_qt) {
+      pair = xcd + kXcds * (local / n_qt);
+      qt = n_qt - 1 - local % n_qt;               // last query tile (most keys) first
+    } else {
+      return;                                     // padding of the grid to a multiple of 8
+    }
+  }
+  const int hs = pair % p.subgroups;
+  const int g = (pair / p.subgroups) % p.num_kv_heads;
+  const int b = pair / (p.subgroups * p.num_kv_heads);
   const int q0 = p.query_start_loc[b];
   const int qb = p.query_start_loc[b + 1] - q0;
   if (qt * p.pos_per_wg >= qb) return;
@@ -350,11 +366,15 @@ hipError_t launch_typed(const PrefillLaunch &a, hipStream_t stream) {
   p.ctx_cap = a.ctx_cap;
   p.num_seqs = a.num_seqs;
   p.scale_log2e = a.scale * kLog2e;
-  const long long gx = (long long)a.num_seqs * a.num_kv_heads * p.subgroups;
-  const int gy = (a.max_query_len + p.pos_per_wg - 1) / p.pos_per_wg;
-  if (gx > 0x7fffffffLL || gy > 65535) return hipErrorInvalidValue;
+  const long long pairs = (long long)a.num_seqs * a.num_kv_heads * p.subgroups;
+  const long long qtiles = (a.max_query_len + p.pos_per_wg - 1) / p.pos_per_wg;
+  // each XCD gets ceil(pairs / 8) pairs' worth of slots
+  const long long grid = kXcds * ((pairs + kXcds - 1) / kXcds) * qtiles;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  p.num_pairs = (int32_t)pairs;
+  p.num_qtiles = (int32_t)qtiles;
   profile_begin(stream);
-  hipLaunchKernelGGL((prefill_kernel<E, D>), dim3((unsigned)gx, gy), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<E, D>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   profile_end(stream);
   return hipGetLastError();
 }
