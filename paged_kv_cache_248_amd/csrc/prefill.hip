@@ -71,6 +71,16 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f
 }
 
 template <class E>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+  if constexpr (__is_same(typename E::storage, _Float16))
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc,
+                                  false);
+  else
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), acc, false);
+}
+
+template <class E>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   if constexpr (__is_same(typename E::storage, _Float16)) return pack_f16(a, b);
   else return pack_bf16(a, b);
@@ -237,6 +247,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   float m = -__builtin_inff();
   float l = 0.f;
   const float c = p.scale_log2e;
+  // packed pair of 1.0 in the storage type
+  const uint32_t ones2 = __is_same(typename E::storage, _Float16) ? 0x3C003C00u : 0x3F803F80u;
 
   // One key tile on the matrix cores: S^T = K Q^T, softmax update, O^T += V^T P^T.
   auto compute = [&](const char *buf, int j) {
@@ -261,12 +273,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
     }
     // Row maximum on raw scores (scale > 0); the scale is folded into the
     // exponent: p = 2^(s*c - m).
-    float rmx = fmaxf(s[0][0], s[0][1]);
+    // (NaN-propagating maximum: lowers to v_maximum3_f32 without the
+    // per-operand canonicalisation an IEEE fmax needs)
+    float rmx = __builtin_elementwise_maximum(s[0][0], s[0][1]);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = (kt == 0 ? 2 : 0); i < 16; i += 2) rmx = fmaxf(rmx, fmaxf(s[kt][i], s[kt][i + 1]));
-    rmx = fmaxf(rmx, shfl_xor(rmx, 32));
+      for (int i = (kt == 0 ? 2 : 0); i < 16; i += 2)
+        rmx = __builtin_elementwise_maximum(rmx, __builtin_elementwise_maximum(s[kt][i], s[kt][i + 1]));
+    rmx = __builtin_elementwise_maximum(rmx, shfl_xor(rmx, 32));
     const float cand = rmx * c;
     if (__any(cand > m + kLazy)) {
       const float m_new = fmaxf(m, cand);
@@ -290,8 +305,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
         for (int q = 0; q < 4; ++q) {
           const float e0 = fast_exp2(fmaf(s[kt][8 * hh + 2 * q], c, nm));
           const float e1 = fast_exp2(fmaf(s[kt][8 * hh + 2 * q + 1], c, nm));
-          l += e0 + e1;
-          w[q] = pack2<E>(e0, e1);
+          const uint32_t pk = pack2<E>(e0, e1);
+          l = dot2<E>(pk, ones2, l);     // L sums the rounded weights PV uses
+          w[q] = pk;
         }
         pf[2 * kt + hh] = w;
       }
