@@ -15,24 +15,37 @@
 //     0..n - q_b + t (bottom-right causal alignment).
 //
 // Design for CDNA4:
-//   * one work-group = 4 wavefronts; each wavefront owns 32 query rows of one
-//     head; the heads of a GQA group sharing a kv head sit in the same
-//     work-group, so each K/V tile staged in LDS serves all of them;
+//   * one work-group = 8 wavefronts in two groups of four; a CU runs one
+//     work-group, so each SIMD holds one wavefront of each group.  Each
+//     wavefront owns 32 query rows of one head; the heads of a GQA group
+//     sharing a kv head sit in the same work-group, so each K/V tile in LDS
+//     serves all of them;
+//   * ping-pong schedule: the key loop runs in phases separated by
+//     work-group barriers.  In every phase one group issues matrix work (QK of
+//     tile j, then PV of tile j-1) while the other group does the softmax of
+//     its last scores; the groups swap roles each phase.  The matrix cores and
+//     the vector ALU of a SIMD are separate units, so the two wavefronts
+//     sharing a SIMD keep both busy;
+//   * K and V tiles go from the paged cache straight into LDS
+//     (global_load_lds_dwordx4, no registers, no LDS write instructions), four
+//     stages each, issued by the matrix group between its MFMAs; completion is
+//     awaited with exact vmcnt counts before the barrier that publishes a
+//     tile, so loads of the next tiles stay in flight across phases;
 //   * per 64-key tile a wavefront computes S^T = K Q^T (2 x D/16 MFMA
 //     32x32x16), so each lane holds one query's scores: the softmax max/sum
 //     stay in-lane except one exchange with the lane 32 apart;
 //   * P^T (bf16/fp16) feeds O^T += V^T P^T (D/32 x 4 MFMA) directly from the
 //     S^T accumulator layout: the MFMA reduction order of the 16 keys of a
 //     k-step is permuted identically in both operands, so no shuffle is needed;
-//   * V is staged transposed in LDS (4-key x 8-dim register transpose with
-//     v_perm), K row-major; both with XOR swizzles that make the MFMA operand
-//     reads and the staging writes bank-conflict free;
-//   * LDS is double buffered: the next tile's global loads are in flight while
-//     the current tile is on the matrix cores; block ids run two tiles ahead;
+//   * K and V are row-major in LDS with XOR swizzles of the 16-byte chunks;
+//     the V^T operand is read with the transposing ds_read_b64_tr_b16; the
+//     operand reads of the next group of four MFMAs are in flight while the
+//     current four execute;
 //   * grid order is XCD-aware: the ids an XCD receives walk one (sequence,
 //     kv head) pair at a time through all its query tiles (the last, with the
 //     most keys, first), so the tiles sharing K/V run together in one L2.
 #include <type_traits>
+#include <utility>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -43,7 +56,8 @@ namespace {
 
 constexpr int kBN = 64;        // keys per tile
 constexpr int kRows = 32;      // query rows per wavefront
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;      // two groups of four
+constexpr int kStages = 4;     // LDS stages per K and per V tile stream
 constexpr int kXcds = 8;       // XCDs of an MI355X; work-group ids are dealt to them round-robin
 
 struct PrefillParams {
@@ -95,25 +109,126 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 // and is conflict-free for those reads.
 __device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) & 7) ^ ((d >> 4) & 1); }
 
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+// Maximum over a lane's 32 scores and those of the lane 32 apart (the two
+// halves of one query's keys), as a depth-4 tree of 3-input maxima; the
+// halves are exchanged with v_permlane32_swap.  NaN-propagating maximum:
+// lowers to v_maximum3_f32 without the per-operand canonicalisation of IEEE
+// fmax.
+__device__ __forceinline__ float row_max(const f32x16 (&s)[2]) {
+  float a[11];
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const int x = 3 * i, y = 3 * i + 1, z = 3 * i + 2;
+    a[i] = max3(s[x >> 4][x & 15], s[y >> 4][y & 15], s[z >> 4][z & 15]);
+  }
+  a[10] = __builtin_elementwise_maximum(s[1][14], s[1][15]);
+  const float b0 = max3(a[0], a[1], a[2]), b1 = max3(a[3], a[4], a[5]);
+  const float b2 = max3(a[6], a[7], a[8]), b3 = __builtin_elementwise_maximum(a[9], a[10]);
+  const float r = __builtin_elementwise_maximum(max3(b0, b1, b2), b3);
+  const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, r),
+                                                   __builtin_bit_cast(uint32_t, r), false, false);
+  return __builtin_elementwise_maximum(__builtin_bit_cast(float, sw[0]),
+                                       __builtin_bit_cast(float, sw[1]));
+}
+
 // Raise the running maximum (and rescale O and L) only when a tile's maximum
 // exceeds it by more than 2^kLazy; weights then stay within [0, 2^kLazy].
 constexpr float kLazy = 8.0f;
 
+// Work-group barrier between phases.  It waits for this wavefront's LDS
+// operations only and keeps the compiler from moving memory accesses or any
+// other instruction across it; direct-to-LDS tile loads stay in flight (their
+// completion is awaited explicitly, with exact counts, before the barrier
+// that publishes a tile).
+__device__ __forceinline__ void phase_sync() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// s_waitcnt vmcnt(N): at most N vector-memory operations of this wavefront
+// still outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One direct-to-LDS load of 1 KB: lane i's 16 bytes at src land at dst + 16 i.
+__device__ __forceinline__ void dma16(const void *src, char *dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+}
+
+// MFMA operand reads from LDS, issued as inline assembly: the compiler does
+// not associate them with the direct-to-LDS loads (whose completion the
+// kernel awaits itself), keeps them in program order with the other volatile
+// statements, and leaves their completion to lds_tie.  Addresses are LDS
+// byte addresses.
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_b128(uint32_t addr) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+  return v;
+}
+// Transposing read (ds_read_b64_tr_b16): in each group of 16 lanes, lane i
+// receives element j from lane 4j + i/4, element i mod 4 of that lane's 8 bytes.
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_tr16(uint32_t addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+  return v;
+}
+// s_waitcnt lgkmcnt(N), tied to the registers it makes valid so that their
+// users stay after it.
+template <int N>
+__device__ __forceinline__ void lds_tie(u32x4 (&r)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) : "i"(N));
+}
+
+// Calls f(integral_constant<int, i>) for i = 0, 1, ... in order.
+template <int... is, class F>
+__device__ __forceinline__ void for_each_index(std::integer_sequence<int, is...>, F &&f) {
+  (f(std::integral_constant<int, is>{}), ...);
+}
+
+// Scalar load of base[idx] (idx uniform), issued where it stands; its value
+// may be used only after sload_tie.  Block-table entries are read this way so
+// that the compiler can neither move the load next to its use (where the
+// wait would also stall the in-flight LDS reads) nor wait on it early.
+__device__ __forceinline__ int sload(const int32_t *base, int idx) {
+  int v;
+  asm volatile("s_load_dword %0, %1, %2" : "=s"(v) : "s"(base), "s"(idx * 4) : "memory");
+  return v;
+}
+
 template <class E, int D>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
-  constexpr int KCH = D / 8;                    // 16-byte chunks per K row
-  constexpr int K_BYTES = kBN * D * 2;          // K tile in LDS
-  constexpr int VT_ROW = kBN * 2;               // bytes per V^T row
-  constexpr int BUF = 2 * K_BYTES;              // K tile + V^T tile
-  constexpr int UNITS = (kBN / 4) * KCH;        // (4 keys x 1 chunk) staging units
+__global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
+  constexpr int KCH = D / 8;                    // 16-byte chunks per row
+  constexpr int ROWB = D * 2;                   // bytes per K or V row in LDS
+  constexpr int TILE = kBN * ROWB;              // one K or V tile
+  constexpr int RPI = 1024 / ROWB;              // rows per 1 KB load instruction
+  constexpr int IPW = 16 / RPI;                 // load instructions per wavefront and tile
   constexpr int KS = D / 16;                    // MFMA k-steps over head_dim
   constexpr int DT = D / 32;                    // 32-wide output sub-tiles
-  static_assert(2 * BUF <= 65536, "LDS offsets must fit the 16-bit immediate");
-  __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
+  constexpr int NS = kStages;
+  // Outstanding vector-memory operations allowed when the tile issued
+  // NS - 2 steps ago must be complete: each step issues IPW tile loads (and
+  // no other vector-memory operation).
+  constexpr int kWaitSteady = (NS - 2) * IPW;
+  extern __shared__ __attribute__((aligned(1024))) char lds[];   // K stages, then V stages
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;      // 0: matrix work in even phases, loads K; 1: odd, loads V
+  const int wi = wave & 3;        // wave within its group; waves wi and wi + 4 share a SIMD
   const int col = lane & 31;      // query column owned by this lane
   const int half = lane >> 5;
 
@@ -139,16 +254,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   const int b = pair / (p.subgroups * p.num_kv_heads);
   const int q0 = p.query_start_loc[b];
   const int qb = p.query_start_loc[b + 1] - q0;
-  if (qt * p.pos_per_wg >= qb) return;
+  if (qt * p.pos_per_wg >= qb) return;            // uniform over the work-group
   const int ctx = min(max(p.context_lens[b], 0), p.ctx_cap);
   const int prefix = ctx - qb;
   const int bs = 1 << p.bs_log2;
   const int npages = (ctx + bs - 1) >> p.bs_log2;
   const int32_t *tbl = p.block_tables + (size_t)b * p.max_blocks_per_seq;
 
+  // Rows: the 32-row blocks of a head alternate between the groups, so both
+  // groups reach the causal diagonal at about the same tile.
   const int hpw = p.heads_per_wg;
-  const int h = g * p.group + hs * hpw + (wave % hpw);
-  const int t0 = qt * p.pos_per_wg + (wave / hpw) * kRows;     // first row of this wavefront
+  const int h = g * p.group + hs * hpw + (wi % hpw);
+  const int t0 = qt * p.pos_per_wg + ((wi / hpw) * 2 + grp) * kRows;
   const int t = t0 + col;                                      // this lane's query row
   const bool row_ok = t < qb;
   const int pos = prefix + t;
@@ -169,193 +286,302 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
     for (int ks = 0; ks < KS; ++ks) qf[ks] = row_ok ? ld16(qp + ks * 32) : u32x4{0u, 0u, 0u, 0u};
   }
 
-  // Per-lane LDS read offsets (the sub-tile / buffer parts are immediates).
-  int k_rd[KS], v_rd[4];
+  // K tile in LDS: row r (key), 16-byte chunk c at position c ^ (r mod KCH).
+  // K operand (A of S^T = K Q^T) read offsets; the 32-key sub-tile is an
+  // immediate.
+  int k_rd[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    k_rd[ks] = col * (D * 2) + (((2 * ks + half) ^ (col & (KCH - 1))) * 16);
-#pragma unroll
-  for (int ks2 = 0; ks2 < 4; ++ks2)
-    v_rd[ks2] = K_BYTES + col * VT_ROW + (((2 * ks2 + half) ^ vt_swz(col)) * 16);
-
-  // Staging unit of this thread: keys 4kg..4kg+3 of the tile, 16-byte chunk dc.
-  const bool stager = tid < UNITS;
-  const int kg = tid / KCH;
-  const int dc = tid % KCH;
-  int k_wr[4], v_wr[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 4 * kg + i;
-    k_wr[i] = row * (D * 2) + ((dc ^ (row & (KCH - 1))) * 16);
-  }
+    k_rd[ks] = col * ROWB + (((2 * ks + half) ^ (col & (KCH - 1))) * 16);
+  // V tile in LDS: row r (key), chunk c at position c ^ vsw(r), vsw(r) =
+  // 4 (r mod 4) for 256-byte rows and 4 ((r / 2) mod 2) for 128-byte rows.
+  // The V^T operand of O^T += V^T P^T is read with ds_read_b64_tr_b16: in
+  // each group of 16 lanes, output lane i takes element j from source lane
+  // 4j + i/4, element i mod 4.  Source lane (G, tt) = (lane / 16, lane % 16)
+  // therefore reads row 4 (G / 2) + tt / 4 of the 8-key half-step at
+  // d = 16 (G mod 2) + 4 (tt mod 4), so that output lane l receives
+  // V[4 (l / 32) + j][l mod 32] for j = 0..3: the four keys MFMA lane l
+  // feeds (the second read, 8 keys later, gives the other four).  The
+  // swizzle makes each 32-lane half of a read hit 16 distinct 16-byte bank
+  // groups; one offset per 32-wide d sub-tile (the key offsets are
+  // immediates).
+  auto vsw = [](int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
+  int v_tr[DT];
   {
-    // the 4 keys land at 16-byte chunk vchunk, byte offset vsub, of each row
-    const int vchunk = 2 * (kg >> 2) + (kg & 1);
-    const int vsub = 8 * ((kg >> 1) & 1);
+    const int G = lane >> 4, tt = lane & 15;
+    const int row = 4 * (G >> 1) + (tt >> 2);
+    const int c0 = 2 * (G & 1) + ((tt & 3) >> 1);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = dc * 8 + e;
-      v_wr[e] = K_BYTES + d * VT_ROW + ((vchunk ^ vt_swz(d)) * 16) + vsub;
-    }
+    for (int dt = 0; dt < DT; ++dt)
+      v_tr[dt] = row * ROWB + (((4 * dt + c0) ^ vsw(row)) * 16) + 8 * (tt & 1);
   }
+
+  // Tile loads: group 0 loads K tiles, group 1 V tiles.  Wave wi of a group
+  // loads rows 16 wi .. 16 wi + 15 of a tile with IPW instructions of RPI
+  // rows; lane i of an instruction fills row i / KCH, position i mod KCH, so
+  // it reads the global chunk (i mod KCH) ^ swizzle(row).  Keys past the
+  // context are read as copies of the last key (same page, as pages hold a
+  // multiple of RPI keys): such keys are masked for every query row, so their
+  // P is 0 and the finite copy adds nothing.
   const size_t head_stride = (size_t)bs * D * 2;
   const size_t block_stride = head_stride * p.num_kv_heads;
-  const char *kb = static_cast<const char *>(p.k_cache) + (size_t)g * head_stride + dc * 16;
-  const char *vb = static_cast<const char *>(p.v_cache) + (size_t)g * head_stride + dc * 16;
-
-  auto fetch_id = [&](int tile) -> int {
-    const int page = (tile * kBN + 4 * kg) >> p.bs_log2;
-    int id = 0;
-    if (stager && tile < ntiles && page < npages) id = tbl[page];
-    return (int)min((unsigned)id, (unsigned)(p.num_blocks - 1));
-  };
-  u32x4 kr[4], vr[4];
-  auto stage = [&](int tile, int id) {
-    const int key0 = tile * kBN + 4 * kg;
-    const bool page_ok = stager && (key0 >> p.bs_log2) < npages;
-    const size_t base = (size_t)id * block_stride + (size_t)(key0 & (bs - 1)) * D * 2;
+  const char *src = static_cast<const char *>(grp == 0 ? p.k_cache : p.v_cache) +
+                    (size_t)g * head_stride;
+  const int klast = max(ctx - 1, 0);
+  const int lrow = lane / KCH;                    // row of this lane within an instruction
+  int lchunk[IPW];                                // global chunk byte offset per instruction
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (page_ok && key0 + i < ctx) {
-        kr[i] = ld16(kb + base + (size_t)i * D * 2);
-        vr[i] = ld16(vb + base + (size_t)i * D * 2);
-      } else {
-        kr[i] = u32x4{0u, 0u, 0u, 0u};
-        vr[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+  for (int q = 0; q < IPW; ++q) {
+    const int r = 16 * wi + RPI * q + lrow;       // row within the tile
+    const int sw = grp == 0 ? (r & (KCH - 1)) : vsw(r);
+    lchunk[q] = ((lane % KCH) ^ sw) * 16;
+  }
+  char *const kbase = lds;
+  char *const vbase = lds + NS * TILE;
+  char *const mybase = grp == 0 ? kbase : vbase;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
+
+  // Block ids of a tile for this wavefront, one per load instruction (the
+  // page of its first row, clamped into the table row), as scalar loads:
+  // they are fetched a phase before use and complete at that phase's
+  // barrier, so they never mix with the tile loads' vector-memory count.
+  struct Ids { int v[IPW]; };
+  auto fetch_ids = [&](int tile) -> Ids {
+    Ids r;
+#pragma unroll
+    for (int q = 0; q < IPW; ++q)
+      r.v[q] = sload(tbl, min((tile * kBN + 16 * wi + RPI * q) >> p.bs_log2, max(npages - 1, 0)));
+    return r;
+  };
+  auto ids_tie = [](Ids &r) {
+    if constexpr (IPW == 4)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(r.v[0]), "+s"(r.v[1]), "+s"(r.v[2]), "+s"(r.v[3]));
+    else
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(r.v[0]), "+s"(r.v[1]));
+  };
+  // Issue instructions [q_lo, q_hi) of the loads of a tile into its stage.
+  auto load_tile = [&](int tile, const Ids &ids, int q_lo, int q_hi) {
+    char *dst = mybase + (tile % NS) * TILE + (16 * wi) * ROWB;
+#pragma unroll
+    for (int q = 0; q < IPW; ++q) {
+      if (q < q_lo || q >= q_hi) continue;
+      const int id = (int)min((unsigned)ids.v[q], (unsigned)(p.num_blocks - 1));
+      const int key = min(tile * kBN + 16 * wi + RPI * q + lrow, klast);
+      const char *gp = src + (size_t)id * block_stride + (size_t)(key & (bs - 1)) * ROWB +
+                       lchunk[q];
+      dma16(gp, dst + RPI * q * ROWB);
     }
   };
-  auto commit = [&](char *buf) {
-    if (!stager) return;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st16(buf + k_wr[i], kr[i]);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t a0 = vr[0][w], a1 = vr[1][w], a2 = vr[2][w], a3 = vr[3][w];
-      const u32x2 even = {__builtin_amdgcn_perm(a1, a0, 0x05040100u),
-                          __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
-      const u32x2 odd = {__builtin_amdgcn_perm(a1, a0, 0x07060302u),
-                         __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
-      *reinterpret_cast<u32x2 *>(buf + v_wr[2 * w]) = even;
-      *reinterpret_cast<u32x2 *>(buf + v_wr[2 * w + 1]) = odd;
-    }
-  };
 
-  f32x16 o[DT];
-#pragma unroll
-  for (int i = 0; i < DT; ++i) o[i] = f32x16{};
-  float m = -__builtin_inff();
-  float l = 0.f;
   const float c = p.scale_log2e;
   // packed pair of 1.0 in the storage type
   const uint32_t ones2 = __is_same(typename E::storage, _Float16) ? 0x3C003C00u : 0x3F803F80u;
 
-  // One key tile on the matrix cores: S^T = K Q^T, softmax update, O^T += V^T P^T.
-  auto compute = [&](const char *buf, int j) {
+  // The whole key loop of one group, specialised on the group so that each
+  // wavefront runs straight-line code with its own register allocation.
+  auto run = [&](auto grp_tag) {
+    constexpr int GRP = decltype(grp_tag)::value;
+    f32x16 o[DT];
+#pragma unroll
+    for (int i = 0; i < DT; ++i) o[i] = f32x16{};
     f32x16 s[2];
+    u32x4 pf[4];
+    float m = -__builtin_inff();
+    float l = 0.f;
+
+    // Matrix phase: S^T = K_j Q^T, then O^T += V^T_{j-1} P^T_{j-1}.  The
+    // MFMAs run in units of four (QK: one 32-key half, 4 k-steps; PV: one
+    // 32-wide d sub-tile); the operand reads of unit u+1 are issued before
+    // the MFMAs of unit u.  `between(kt)` issues tile loads after QK half kt.
+    constexpr int QU = KS / 4 * 2;                // QK units
+    constexpr int U = QU + DT;                    // all units
+    auto matrix_phase = [&](uint32_t kb, uint32_t vb, bool do_pv, auto &&between) {
+      u32x4 R[2][4];
+      auto issue = [&](auto u_tag) {
+        constexpr int u = decltype(u_tag)::value;
+        u32x4(&r)[4] = R[u & 1];
+        if constexpr (u < QU) {
+          constexpr int kt = u / (KS / 4), ks0 = 4 * (u % (KS / 4));
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      f32x16 acc = mfma32<E>(ld16(buf + k_rd[0] + kt * 32 * D * 2), qf[0], f32x16{});
+          for (int i = 0; i < 4; ++i) r[i] = lds_b128<kt * 32 * ROWB>(kb + k_rd[ks0 + i]);
+        } else {
+          constexpr int dt = u - QU;
+          const uint32_t a = vb + v_tr[dt];
+          // keys 16 ks2 + 4h + 0..3 and 16 ks2 + 8 + 4h + 0..3 of the tile
+          const u32x2 l0 = lds_tr16<0 * ROWB>(a), h0 = lds_tr16<8 * ROWB>(a);
+          const u32x2 l1 = lds_tr16<16 * ROWB>(a), h1 = lds_tr16<24 * ROWB>(a);
+          const u32x2 l2 = lds_tr16<32 * ROWB>(a), h2 = lds_tr16<40 * ROWB>(a);
+          const u32x2 l3 = lds_tr16<48 * ROWB>(a), h3 = lds_tr16<56 * ROWB>(a);
+          r[0] = u32x4{l0[0], l0[1], h0[0], h0[1]};
+          r[1] = u32x4{l1[0], l1[1], h1[0], h1[1]};
+          r[2] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+          r[3] = u32x4{l3[0], l3[1], h3[0], h3[1]};
+        }
+      };
+      auto consume = [&](auto u_tag) {
+        constexpr int u = decltype(u_tag)::value;
+        u32x4(&r)[4] = R[u & 1];
+        if constexpr (u < QU) {
+          constexpr int kt = u / (KS / 4), ks0 = 4 * (u % (KS / 4));
+          f32x16 acc = ks0 == 0 ? f32x16{} : s[kt];
 #pragma unroll
-      for (int ks = 1; ks < KS; ++ks)
-        acc = mfma32<E>(ld16(buf + k_rd[ks] + kt * 32 * D * 2), qf[ks], acc);
-      s[kt] = acc;
-    }
-    // Causal mask where the tile can reach past this wavefront's first
-    // position: key (tile offset kt*32 + 8*(i/4) + 4*half + i%4) > position.
-    if (j * kBN + kBN - 1 > prefix + t0) {
-      const int lim = pos - (j * kBN + 4 * half);
+          for (int i = 0; i < 4; ++i) acc = mfma32<E>(r[i], qf[ks0 + i], acc);
+          s[kt] = acc;
+        } else {
+          constexpr int dt = u - QU;
+#pragma unroll
+          for (int ks2 = 0; ks2 < 4; ++ks2) o[dt] = mfma32<E>(r[ks2], pf[ks2], o[dt]);
+        }
+      };
+      auto pipeline = [&](auto n_tag) {
+        constexpr int N = decltype(n_tag)::value;   // units run: QU (QK only) or U
+        issue(std::integral_constant<int, 0>{});
+        for_each_index(std::make_integer_sequence<int, N>{}, [&](auto u_tag) {
+            constexpr int u = decltype(u_tag)::value;
+            if constexpr (u + 1 < N) {
+              issue(std::integral_constant<int, u + 1>{});
+              constexpr int next_ops = u + 1 < QU ? 4 : 8;
+              lds_tie<next_ops>(R[u & 1]);
+            } else {
+              lds_tie<0>(R[u & 1]);
+            }
+            consume(std::integral_constant<int, u>{});
+            if constexpr (u < QU && (u + 1) % (KS / 4) == 0) {
+              __builtin_amdgcn_sched_barrier(0);
+              between(u / (KS / 4));
+              __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+      };
+      if (do_pv) pipeline(std::integral_constant<int, U>{});
+      else pipeline(std::integral_constant<int, QU>{});
+    };
+
+    // Softmax of tile j's scores: online update of (m, l, O) and the P^T
+    // fragments for the next matrix phase.
+    auto softmax = [&](int j) {
+      // Causal mask where the tile can reach past this wavefront's first
+      // position: key (tile offset kt*32 + 8*(i/4) + 4*half + i%4) > position.
+      if (j * kBN + kBN - 1 > prefix + t0) {
+        const int lim = pos - (j * kBN + 4 * half);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            s[kt][i] = (kt * 32 + 8 * (i >> 2) + (i & 3)) > lim ? -__builtin_inff() : s[kt][i];
+      }
+      // Row maximum on raw scores (scale > 0); the scale is folded into the
+      // exponent: p = 2^(s*c - m).
+      const float rmx = row_max(s);
+      const float cand = rmx * c;
+      if (__any(cand > m + kLazy)) {
+        const float m_new = fmaxf(m, cand);
+        const float alpha = m_new > m ? fast_exp2(m - m_new) : 1.0f;
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < DT; ++i) o[i] *= alpha;
+        m = m_new;
+      }
+      // A row with every key so far masked keeps m = -inf; use 0 as its
+      // reference so its weights come out 0 instead of NaN.
+      const float nm = m == -__builtin_inff() ? 0.f : -m;
+      // P^T fragments: k-step ks2 = 2kt + hh takes accumulator entries 8hh..8hh+7.
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          s[kt][i] = (kt * 32 + 8 * (i >> 2) + (i & 3)) > lim ? -__builtin_inff() : s[kt][i];
-    }
-    // Row maximum on raw scores (scale > 0); the scale is folded into the
-    // exponent: p = 2^(s*c - m).
-    // (NaN-propagating maximum: lowers to v_maximum3_f32 without the
-    // per-operand canonicalisation an IEEE fmax needs)
-    float rmx = __builtin_elementwise_maximum(s[0][0], s[0][1]);
+        for (int hh = 0; hh < 2; ++hh) {
+          u32x4 w;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = (kt == 0 ? 2 : 0); i < 16; i += 2)
-        rmx = __builtin_elementwise_maximum(rmx, __builtin_elementwise_maximum(s[kt][i], s[kt][i + 1]));
-    rmx = __builtin_elementwise_maximum(rmx, shfl_xor(rmx, 32));
-    const float cand = rmx * c;
-    if (__any(cand > m + kLazy)) {
-      const float m_new = fmaxf(m, cand);
-      const float alpha = m_new > m ? fast_exp2(m - m_new) : 1.0f;
-      l *= alpha;
-#pragma unroll
-      for (int i = 0; i < DT; ++i) o[i] *= alpha;
-      m = m_new;
-    }
-    // A row with every key so far masked keeps m = -inf; use 0 as its
-    // reference so its weights come out 0 instead of NaN.
-    const float nm = m == -__builtin_inff() ? 0.f : -m;
-    // P^T fragments: k-step ks2 = 2kt + hh takes accumulator entries 8hh..8hh+7.
-    u32x4 pf[4];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        u32x4 w;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float e0 = fast_exp2(fmaf(s[kt][8 * hh + 2 * q], c, nm));
-          const float e1 = fast_exp2(fmaf(s[kt][8 * hh + 2 * q + 1], c, nm));
-          const uint32_t pk = pack2<E>(e0, e1);
-          l = dot2<E>(pk, ones2, l);     // L sums the rounded weights PV uses
-          w[q] = pk;
+          for (int q = 0; q < 4; ++q) {
+            const float e0 = fast_exp2(fmaf(s[kt][8 * hh + 2 * q], c, nm));
+            const float e1 = fast_exp2(fmaf(s[kt][8 * hh + 2 * q + 1], c, nm));
+            const uint32_t pk = pack2<E>(e0, e1);
+            l = dot2<E>(pk, ones2, l);     // L sums the rounded weights PV uses
+            w[q] = pk;
+          }
+          pf[2 * kt + hh] = w;
         }
-        pf[2 * kt + hh] = w;
+    };
+
+    // Prologue.  Group 0 loads K_0 .. K_{NS-2} and waits for K_0; group 1
+    // loads V_0 .. V_{NS-3}.  Each then holds the block ids of its next tile.
+    // `ids` holds the block ids of the tile this group loads in its next
+    // matrix phase; they are fetched in the phase before it.
+    Ids ids;
+    wait_vm<0>();                                 // query fragments in registers
+    if constexpr (GRP == 0) {
+#pragma unroll
+      for (int tt = 0; tt < NS - 1; ++tt) {
+        Ids pre = fetch_ids(tt);
+        ids_tie(pre);
+        load_tile(tt, pre, 0, IPW);
       }
+      ids = fetch_ids(NS - 1);
+      ids_tie(ids);
+      wait_vm<IPW * (NS - 2)>();
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < NS - 2; ++tt) {
+        Ids pre = fetch_ids(tt);
+        ids_tie(pre);
+        load_tile(tt, pre, 0, IPW);
+      }
+    }
+    phase_sync();
+
+    // Step j = phases 2j and 2j+1.  In both, the matrix group reads K_j (K
+    // stage j % NS) and V_{j-1} (V stage (j-1) % NS).  Group 0 loads
+    // K_{j+NS-1} in phase 2j and, before the barrier that ends phase 2j+1,
+    // waits for K_{j+1}; group 1 loads V_{j+NS-2} in phase 2j+1 and waits for
+    // V_j before the barrier that ends it.  A stage is refilled only after
+    // the barrier that ends the last phase reading it.
+    for (int j = 0; j <= ntiles; ++j) {
+      const uint32_t kb = lds0 + (j % NS) * TILE;
+      const uint32_t vb = lds0 + (NS + (j + NS - 1) % NS) * TILE;
+      const bool qk = j < wave_tiles;
+      const bool pv = j >= 1 && j - 1 < wave_tiles;
+      const int lt = GRP == 0 ? j + NS - 1 : j + NS - 2;     // tile loaded this step
+      auto between = [&](int kt) {
+        if (kt == 0) load_tile(lt, ids, 0, IPW / 2);
+        else load_tile(lt, ids, IPW / 2, IPW);
+      };
+      if constexpr (GRP == 0) {
+        matrix_phase(kb, vb, pv, between);                // phase 2j
+        phase_sync();
+        ids = fetch_ids(lt + 1);                          // phase 2j+1
+        if (qk) softmax(j);
+        ids_tie(ids);
+        wait_vm<kWaitSteady>();
+        phase_sync();
+      } else {
+        ids = fetch_ids(lt);                              // phase 2j
+        if (pv) softmax(j - 1);
+        ids_tie(ids);
+        phase_sync();
+        matrix_phase(kb, vb, pv, between);                // phase 2j+1
+        wait_vm<kWaitSteady>();
+        phase_sync();
+      }
+    }
+    // No tile load may still be writing this work-group's LDS when it exits.
+    wait_vm<0>();
+
+    if (!row_ok || wave_tiles == 0) return;
+    const float lt = l + shfl_xor(l, 32);
+    const float inv = 1.0f / lt;
+    char *op = static_cast<char *>(p.out) + ((size_t)(q0 + t) * p.num_heads + h) * D * 2;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int ks2 = 0; ks2 < 4; ++ks2)
-        o[dt] = mfma32<E>(ld16(buf + v_rd[ks2] + dt * 32 * VT_ROW), pf[ks2], o[dt]);
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = dt * 32 + 8 * r4 + 4 * half;
+        const u32x2 v = {pack2<E>(o[dt][4 * r4] * inv, o[dt][4 * r4 + 1] * inv),
+                         pack2<E>(o[dt][4 * r4 + 2] * inv, o[dt][4 * r4 + 3] * inv)};
+        *reinterpret_cast<u32x2 *>(op + d * 2) = v;
+      }
   };
-
-  int id_next = fetch_id(0);
-  stage(0, id_next);
-  id_next = fetch_id(1);
-  int id_after = fetch_id(2);
-  commit(lds);
-  __syncthreads();
-
-  // Tile j uses buffer j % 2; the loop is unrolled by two so every LDS
-  // offset is a compile-time immediate.
-  auto step = [&](auto cur_tag, int j) {
-    constexpr int CUR = decltype(cur_tag)::value;
-    if (j + 1 < ntiles) {
-      stage(j + 1, id_next);
-      id_next = id_after;
-      id_after = fetch_id(j + 3);
-    }
-    if (j < wave_tiles) compute(lds + CUR * BUF, j);
-    if (j + 1 < ntiles) commit(lds + (CUR ^ 1) * BUF);
-    __syncthreads();
-  };
-  for (int j = 0; j < ntiles; j += 2) {
-    step(std::integral_constant<int, 0>{}, j);
-    if (j + 1 < ntiles) step(std::integral_constant<int, 1>{}, j + 1);
-  }
-
-  if (!row_ok || wave_tiles == 0) return;
-  const float lt = l + shfl_xor(l, 32);
-  const float inv = 1.0f / lt;
-  char *op = static_cast<char *>(p.out) + ((size_t)(q0 + t) * p.num_heads + h) * D * 2;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int d = dt * 32 + 8 * r + 4 * half;
-      const u32x2 v = {pack2<E>(o[dt][4 * r] * inv, o[dt][4 * r + 1] * inv),
-                       pack2<E>(o[dt][4 * r + 2] * inv, o[dt][4 * r + 3] * inv)};
-      *reinterpret_cast<u32x2 *>(op + d * 2) = v;
-    }
+  if (grp == 0) run(std::integral_constant<int, 0>{});
+  else run(std::integral_constant<int, 1>{});
 }
 
 template <class E, int D>
@@ -389,8 +615,18 @@ hipError_t launch_typed(const PrefillLaunch &a, hipStream_t stream) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   p.num_pairs = (int32_t)pairs;
   p.num_qtiles = (int32_t)qtiles;
+  const size_t lds_bytes = (size_t)2 * kStages * 64 * D * 2;
+  static bool attr_set = false;   // per instantiation; the attribute is per function
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_kernel<E, D>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)lds_bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
   profile_begin(stream);
-  hipLaunchKernelGGL((prefill_kernel<E, D>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<E, D>), dim3((unsigned)grid), dim3(64 * kWaves), lds_bytes,
+                     stream, p);
   profile_end(stream);
   return hipGetLastError();
 }
