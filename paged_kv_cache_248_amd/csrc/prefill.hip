@@ -58,6 +58,7 @@ constexpr int kBN = 64;        // keys per tile
 constexpr int kRows = 32;      // query rows per wavefront
 constexpr int kWaves = 8;      // two groups of four
 constexpr int kStages = 4;     // LDS stages per K and per V tile stream
+constexpr int kReadAhead = 1;  // MFMA operand units whose LDS reads are in flight
 constexpr int kXcds = 8;       // XCDs of an MI355X; work-group ids are dealt to them round-robin
 
 struct PrefillParams {
@@ -396,10 +397,11 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
     constexpr int QU = KS / 4 * 2;                // QK units
     constexpr int U = QU + DT;                    // all units
     auto matrix_phase = [&](uint32_t kb, uint32_t vb, bool do_pv, auto &&between) {
-      u32x4 R[2][4];
+      constexpr int AHEAD = kReadAhead;
+      u32x4 R[AHEAD + 1][4];
       auto issue = [&](auto u_tag) {
         constexpr int u = decltype(u_tag)::value;
-        u32x4(&r)[4] = R[u & 1];
+        u32x4(&r)[4] = R[u % (AHEAD + 1)];
         if constexpr (u < QU) {
           constexpr int kt = u / (KS / 4), ks0 = 4 * (u % (KS / 4));
 #pragma unroll
@@ -420,7 +422,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
       };
       auto consume = [&](auto u_tag) {
         constexpr int u = decltype(u_tag)::value;
-        u32x4(&r)[4] = R[u & 1];
+        u32x4(&r)[4] = R[u % (AHEAD + 1)];
         if constexpr (u < QU) {
           constexpr int kt = u / (KS / 4), ks0 = 4 * (u % (KS / 4));
           f32x16 acc = ks0 == 0 ? f32x16{} : s[kt];
@@ -435,16 +437,21 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
       };
       auto pipeline = [&](auto n_tag) {
         constexpr int N = decltype(n_tag)::value;   // units run: QU (QK only) or U
-        issue(std::integral_constant<int, 0>{});
+        // LDS reads of a unit: 4 (K) or 8 (V^T halves)
+        constexpr auto ops = [](int v) { return v < QU ? 4 : 8; };
+        for_each_index(std::make_integer_sequence<int, (AHEAD < N ? AHEAD : N)>{},
+                       [&](auto u_tag) { issue(u_tag); });
         for_each_index(std::make_integer_sequence<int, N>{}, [&](auto u_tag) {
             constexpr int u = decltype(u_tag)::value;
-            if constexpr (u + 1 < N) {
-              issue(std::integral_constant<int, u + 1>{});
-              constexpr int next_ops = u + 1 < QU ? 4 : 8;
-              lds_tie<next_ops>(R[u & 1]);
-            } else {
-              lds_tie<0>(R[u & 1]);
-            }
+            if constexpr (u + AHEAD < N) issue(std::integral_constant<int, u + AHEAD>{});
+            // reads issued after unit u's: those of units u+1 .. min(u+AHEAD, N-1)
+            constexpr int later = [&] {
+              int n = 0;
+              for (int v = u + 1; v <= u + AHEAD && v < N; ++v) n += ops(v);
+              return n;
+            }();
+            // (lgkmcnt holds at most 15: waiting for fewer is only stricter)
+            lds_tie<(later < 15 ? later : 15)>(R[u % (AHEAD + 1)]);
             consume(std::integral_constant<int, u>{});
             if constexpr (u < QU && (u + 1) % (KS / 4) == 0) {
               __builtin_amdgcn_sched_barrier(0);
