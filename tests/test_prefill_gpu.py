@@ -54,6 +54,25 @@ def test_prefill_small_against_oracle(dtype, D, Hq, Hkv, bs):
     log(f"  max rel err {e:.3e}")
 
 
+BLOCK_SIZES = [(dtype, D, bs) for dtype in ("f16", "bf16") for D in (64, 128)
+               for bs in (8, 64, 128, 256)]
+
+
+@pytest.mark.parametrize("dtype,D,bs", BLOCK_SIZES)
+def test_prefill_block_sizes(dtype, D, bs):
+    """Pages smaller than a wavefront's 16 keys of a tile (8) and larger than a
+    64-key tile (128, 256): block ids per load instruction and slot offsets
+    that change from tile to tile inside one page; contexts ending mid-page."""
+    rng = np.random.default_rng(zlib.crc32(repr(("prefill-bs", dtype, D, bs)).encode()))
+    ql = np.array([3, 64, 129, int(rng.integers(40, 260))])
+    pre = np.array([int(rng.integers(0, 9)), 250, int(rng.integers(300, 700)), 1])
+    log(f"prefill block size dtype={dtype} D={D} bs={bs} pre={pre.tolist()} q={ql.tolist()}")
+    case = wl.make_prefill(pre, ql, 8, 2, D, bs, dtype, seed=int(rng.integers(1 << 30)),
+                           device=DEV, poison=True)
+    e = assert_close(host(run_prefill(case)), oracle_full(case), dtype, "prefill block size")
+    log(f"  max rel err {e:.3e}")
+
+
 def test_prefill_no_prefix_is_plain_causal():
     case = wl.make_prefill([0, 0], [200, 64], 8, 2, 128, 16, "bf16", seed=3, device=DEV)
     assert_close(host(run_prefill(case)), oracle_full(case), "bf16", "no prefix")
