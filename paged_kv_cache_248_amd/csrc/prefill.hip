@@ -86,16 +86,6 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f
 }
 
 template <class E>
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
-  if constexpr (__is_same(typename E::storage, _Float16))
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc,
-                                  false);
-  else
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
-                                           __builtin_bit_cast(bf16x2, b), acc, false);
-}
-
-template <class E>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   if constexpr (__is_same(typename E::storage, _Float16)) return pack_f16(a, b);
   else return pack_bf16(a, b);
@@ -140,14 +130,14 @@ __device__ __forceinline__ float row_max(const f32x16 (&s)[2]) {
 // exceeds it by more than 2^kLazy; weights then stay within [0, 2^kLazy].
 constexpr float kLazy = 8.0f;
 
-// Work-group barrier between phases.  It waits for this wavefront's LDS
-// operations only and keeps the compiler from moving memory accesses or any
-// other instruction across it; direct-to-LDS tile loads stay in flight (their
-// completion is awaited explicitly, with exact counts, before the barrier
-// that publishes a tile).
+// Work-group barrier between phases.  It keeps the compiler from moving
+// memory accesses or any other instruction across it and waits for nothing:
+// every LDS read of the loop is consumed (so complete) before its phase ends,
+// LDS is written only by the direct-to-LDS tile loads, whose completion is
+// awaited explicitly with exact counts before the barrier that publishes a
+// tile, and block-id scalar loads may stay in flight across it.
 __device__ __forceinline__ void phase_sync() {
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0)
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -330,12 +320,17 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
                     (size_t)g * head_stride;
   const int klast = max(ctx - 1, 0);
   const int lrow = lane / KCH;                    // row of this lane within an instruction
-  int lchunk[IPW];                                // global chunk byte offset per instruction
+  // Per instruction q: the global chunk byte offset of this lane, and its
+  // byte offset within the page for tiles that lie inside the context (row
+  // r of tile t is key 64 t + r, in slot (64 t mod bs) + (r mod min(bs, 64))).
+  int lchunk[IPW], lane_off[IPW];
+  const int rmask = min(bs, kBN) - 1;
 #pragma unroll
   for (int q = 0; q < IPW; ++q) {
     const int r = 16 * wi + RPI * q + lrow;       // row within the tile
     const int sw = grp == 0 ? (r & (KCH - 1)) : vsw(r);
     lchunk[q] = ((lane % KCH) ^ sw) * 16;
+    lane_off[q] = (r & rmask) * ROWB + lchunk[q];
   }
   char *const kbase = lds;
   char *const vbase = lds + NS * TILE;
@@ -344,39 +339,50 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
 
   // Block ids of a tile for this wavefront, one per load instruction (the
   // page of its first row, clamped into the table row), as scalar loads:
-  // they are fetched a phase before use and complete at that phase's
-  // barrier, so they never mix with the tile loads' vector-memory count.
-  struct Ids { int v[IPW]; };
+  // they are issued at the start of the softmax phase before the matrix
+  // phase that uses them and awaited at the start of that matrix phase,
+  // before any of its LDS reads (scalar and LDS loads share one counter and
+  // scalar loads complete out of order, so the wait is for all of them).
+  // A wavefront's 16 rows of a tile lie in at most two pages (rows 0-7 and
+  // 8-15 of its part share a page, as pages hold at least 8 keys): ids.v[h]
+  // is the entry of the page of row 16 wi + 8 h.
+  struct Ids { int v[2]; };
   auto fetch_ids = [&](int tile) -> Ids {
     Ids r;
 #pragma unroll
-    for (int q = 0; q < IPW; ++q)
-      r.v[q] = sload(tbl, min((tile * kBN + 16 * wi + RPI * q) >> p.bs_log2, max(npages - 1, 0)));
+    for (int hh = 0; hh < 2; ++hh)
+      r.v[hh] = sload(tbl, min((tile * kBN + 16 * wi + 8 * hh) >> p.bs_log2, max(npages - 1, 0)));
     return r;
   };
   auto ids_tie = [](Ids &r) {
-    if constexpr (IPW == 4)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(r.v[0]), "+s"(r.v[1]), "+s"(r.v[2]), "+s"(r.v[3]));
-    else
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(r.v[0]), "+s"(r.v[1]));
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(r.v[0]), "+s"(r.v[1]));
   };
   // Issue instructions [q_lo, q_hi) of the loads of a tile into its stage.
   auto load_tile = [&](int tile, const Ids &ids, int q_lo, int q_hi) {
     char *dst = mybase + (tile % NS) * TILE + (16 * wi) * ROWB;
+    const char *base[2];
 #pragma unroll
-    for (int q = 0; q < IPW; ++q) {
-      if (q < q_lo || q >= q_hi) continue;
-      const int id = (int)min((unsigned)ids.v[q], (unsigned)(p.num_blocks - 1));
-      const int key = min(tile * kBN + 16 * wi + RPI * q + lrow, klast);
-      const char *gp = src + (size_t)id * block_stride + (size_t)(key & (bs - 1)) * ROWB +
-                       lchunk[q];
-      dma16(gp, dst + RPI * q * ROWB);
+    for (int hh = 0; hh < 2; ++hh)
+      base[hh] = src + (size_t)min((unsigned)ids.v[hh], (unsigned)(p.num_blocks - 1)) * block_stride;
+    if (tile * kBN + kBN <= ctx) {                // every key of the tile exists
+      const uint32_t toff = (uint32_t)((tile * kBN) & (bs - 1)) * ROWB;
+#pragma unroll
+      for (int q = 0; q < IPW; ++q) {
+        if (q < q_lo || q >= q_hi) continue;
+        dma16(base[RPI * q / 8] + (toff + lane_off[q]), dst + RPI * q * ROWB);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < IPW; ++q) {
+        if (q < q_lo || q >= q_hi) continue;
+        const int key = min(tile * kBN + 16 * wi + RPI * q + lrow, klast);
+        dma16(base[RPI * q / 8] + ((uint32_t)(key & (bs - 1)) * ROWB + lchunk[q]),
+              dst + RPI * q * ROWB);
+      }
     }
   };
 
   const float c = p.scale_log2e;
-  // packed pair of 1.0 in the storage type
-  const uint32_t ones2 = __is_same(typename E::storage, _Float16) ? 0x3C003C00u : 0x3F803F80u;
 
   // The whole key loop of one group, specialised on the group so that each
   // wavefront runs straight-line code with its own register allocation.
@@ -493,6 +499,12 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
       // reference so its weights come out 0 instead of NaN.
       const float nm = m == -__builtin_inff() ? 0.f : -m;
       // P^T fragments: k-step ks2 = 2kt + hh takes accumulator entries 8hh..8hh+7.
+      // L adds the fp32 weights in four partial sums (plain VALU adds: the
+      // dot2 instructions would not overlap with the other wavefront's MFMAs
+      // on this SIMD); rounding P to 16 bits for PV is unbiased, so the
+      // normalised output differs from summing the rounded weights only by
+      // that rounding noise.
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -502,12 +514,12 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
           for (int q = 0; q < 4; ++q) {
             const float e0 = fast_exp2(fmaf(s[kt][8 * hh + 2 * q], c, nm));
             const float e1 = fast_exp2(fmaf(s[kt][8 * hh + 2 * q + 1], c, nm));
-            const uint32_t pk = pack2<E>(e0, e1);
-            l = dot2<E>(pk, ones2, l);     // L sums the rounded weights PV uses
-            w[q] = pk;
+            ls[q] += e0 + e1;
+            w[q] = pack2<E>(e0, e1);
           }
           pf[2 * kt + hh] = w;
         }
+      l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     };
 
     // Prologue.  Group 0 loads K_0 .. K_{NS-2} and waits for K_0; group 1
@@ -553,19 +565,19 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
         else load_tile(lt, ids, IPW / 2, IPW);
       };
       if constexpr (GRP == 0) {
-        matrix_phase(kb, vb, pv, between);                // phase 2j
+        ids_tie(ids);                                     // phase 2j
+        matrix_phase(kb, vb, pv, between);
         phase_sync();
         ids = fetch_ids(lt + 1);                          // phase 2j+1
         if (qk) softmax(j);
-        ids_tie(ids);
         wait_vm<kWaitSteady>();
         phase_sync();
       } else {
         ids = fetch_ids(lt);                              // phase 2j
         if (pv) softmax(j - 1);
-        ids_tie(ids);
         phase_sync();
-        matrix_phase(kb, vb, pv, between);                // phase 2j+1
+        ids_tie(ids);                                     // phase 2j+1
+        matrix_phase(kb, vb, pv, between);
         wait_vm<kWaitSteady>();
         phase_sync();
       }
