@@ -271,17 +271,24 @@ __global__ __launch_bounds__(256, GT == 4 ? 4 : 2) void decode_kernel(DecodePara
         }
       }
     };
+    const float c = p.scale_log2e;
     auto consume = [&](int t, const u32x4 *kr, const u32x4 *vr) {
       const int ts = tile_start(t);
+      const bool tail = ts + TILE > end;     // only the last tile can hold rows past the end
+      // Scores in log2 units.  (Subtracting the running maximum from the
+      // scaled score keeps a lone maximal key's weight exactly 1.)
       float x[GT][NL];
 #pragma unroll
-      for (int L = 0; L < NL; ++L) {
-        const bool valid = ts + L * TPL + tok < end;
+      for (int L = 0; L < NL; ++L)
 #pragma unroll
-        for (int j = 0; j < GT; ++j) {
-          const float s = group_sum<LPT>(dot16<E>(q[j], kr[L]));
-          x[j][L] = valid ? s * p.scale_log2e : -__builtin_inff();
-        }
+        for (int j = 0; j < GT; ++j) x[j][L] = group_sum<LPT>(dot16<E>(q[j], kr[L])) * c;
+      if (tail) {
+#pragma unroll
+        for (int L = 0; L < NL; ++L)
+          if (ts + L * TPL + tok >= end) {
+#pragma unroll
+            for (int j = 0; j < GT; ++j) x[j][L] = -__builtin_inff();
+          }
       }
 #pragma unroll
       for (int j = 0; j < GT; ++j) {
@@ -302,7 +309,6 @@ __global__ __launch_bounds__(256, GT == 4 ? 4 : 2) void decode_kernel(DecodePara
           l[j] += x[j][L];
         }
       }
-      const bool tail = ts + TILE > end;     // only the last tile can hold rows past the end
 #pragma unroll
       for (int L = 0; L < NL; ++L) {
         float vf[EPL];

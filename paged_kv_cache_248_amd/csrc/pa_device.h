@@ -70,6 +70,29 @@ constexpr int kDppXor2 = 0x4E;
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
 
+// Value of the lane 8 apart inside a row (row_ror:8: lane i reads lane
+// (i + 8) mod 16 of its row, which is i ^ 8).
+constexpr int kDppRor8 = 0x128;
+
+// The values of lanes l and l ^ 16 (l ^ 32) as a pair, by one VALU permute
+// (v_permlane16_swap / v_permlane32_swap of two copies of the value).  Both
+// lanes of a pair receive the two values in the same order, so a sum of the
+// pair is bit-identical on both.  (The two results are copied to scalars
+// before the bit cast: a bit cast of an indexed vector element miscompiles,
+// every index reading element 0.)
+__device__ __forceinline__ f32x2 pair_xor16(float v) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  return f32x2{__uint_as_float(r0), __uint_as_float(r1)};
+}
+__device__ __forceinline__ f32x2 pair_xor32(float v) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  return f32x2{__uint_as_float(r0), __uint_as_float(r1)};
+}
+
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
   const int lane = __lane_id();
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
@@ -85,8 +108,8 @@ __device__ __forceinline__ float group_sum(float v) {
   v += dpp<kDppXor2>(v);
   v += dpp<kDppHalfMirror>(v);
   if constexpr (N >= 16) v += dpp<kDppMirror>(v);
-  if constexpr (N >= 32) v += shfl_xor(v, 16);
-  if constexpr (N >= 64) v += shfl_xor(v, 32);
+  if constexpr (N >= 32) { const f32x2 r = pair_xor16(v); v = r[0] + r[1]; }
+  if constexpr (N >= 64) { const f32x2 r = pair_xor32(v); v = r[0] + r[1]; }
   return v;
 }
 
@@ -94,18 +117,18 @@ __device__ __forceinline__ float group_sum(float v) {
 // the 64/STRIDE groups of STRIDE lanes).  STRIDE = 64 is a no-op.
 template <int STRIDE>
 __device__ __forceinline__ float across_groups_max(float v) {
-  if constexpr (STRIDE <= 16) v = fmaxf(v, shfl_xor(v, 16));
-  if constexpr (STRIDE <= 8) v = fmaxf(v, shfl_xor(v, 8));
-  if constexpr (STRIDE <= 32) v = fmaxf(v, shfl_xor(v, 32));
+  if constexpr (STRIDE <= 8) v = fmaxf(v, dpp<kDppRor8>(v));
+  if constexpr (STRIDE <= 16) { const f32x2 r = pair_xor16(v); v = fmaxf(r[0], r[1]); }
+  if constexpr (STRIDE <= 32) { const f32x2 r = pair_xor32(v); v = fmaxf(r[0], r[1]); }
   return v;
 }
 
 template <int STRIDE>
 __device__ __forceinline__ float across_groups_sum(float v) {
-  // Fixed order so every lane computes the same association.
-  if constexpr (STRIDE <= 8) v += shfl_xor(v, 8);
-  if constexpr (STRIDE <= 16) v += shfl_xor(v, 16);
-  if constexpr (STRIDE <= 32) v += shfl_xor(v, 32);
+  // Every lane of an exchanged pair adds the same two operands.
+  if constexpr (STRIDE <= 8) v += dpp<kDppRor8>(v);
+  if constexpr (STRIDE <= 16) { const f32x2 r = pair_xor16(v); v = r[0] + r[1]; }
+  if constexpr (STRIDE <= 32) { const f32x2 r = pair_xor32(v); v = r[0] + r[1]; }
   return v;
 }
 

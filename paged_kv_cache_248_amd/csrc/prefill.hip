@@ -120,10 +120,8 @@ __device__ __forceinline__ float row_max(const f32x16 (&s)[2]) {
   const float b0 = max3(a[0], a[1], a[2]), b1 = max3(a[3], a[4], a[5]);
   const float b2 = max3(a[6], a[7], a[8]), b3 = __builtin_elementwise_maximum(a[9], a[10]);
   const float r = __builtin_elementwise_maximum(max3(b0, b1, b2), b3);
-  const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, r),
-                                                   __builtin_bit_cast(uint32_t, r), false, false);
-  return __builtin_elementwise_maximum(__builtin_bit_cast(float, sw[0]),
-                                       __builtin_bit_cast(float, sw[1]));
+  const f32x2 sw = pair_xor32(r);
+  return __builtin_elementwise_maximum(sw[0], sw[1]);
 }
 
 // Raise the running maximum (and rescale O and L) only when a tile's maximum

@@ -73,6 +73,26 @@ def test_prefill_block_sizes(dtype, D, bs):
     log(f"  max rel err {e:.3e}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_large_score_gap_inside_a_tile(dtype):
+    """Keys 4..7 of every 8 score about 255 log2 units above the others.  In
+    the S^T accumulator those keys sit in the other half of the wavefront
+    (lane l vs l + 32), so the row maximum must combine both halves: a
+    maximum over one half only would overflow exp2 on the other."""
+    ql = np.array([40, 100])
+    pre = np.array([30, 200])
+    case = wl.make_prefill(pre, ql, 8, 2, 128, 16, dtype, seed=11, device=DEV)
+    kv = case.kv
+    slots = torch.arange(kv.k_cache.shape[2], device=DEV)
+    big = (slots % 8 >= 4).view(1, 1, -1, 1)
+    kv.k_cache.copy_(torch.where(big, torch.full_like(kv.k_cache, 4.0),
+                                 torch.full_like(kv.k_cache, 0.1)))
+    case.query.fill_(4.0)
+    out = run_prefill(case)
+    assert torch.isfinite(out.float()).all()
+    assert_close(host(out), oracle_full(case), dtype, "prefill score gap")
+
+
 def test_prefill_no_prefix_is_plain_causal():
     case = wl.make_prefill([0, 0], [200, 64], 8, 2, 128, 16, "bf16", seed=3, device=DEV)
     assert_close(host(run_prefill(case)), oracle_full(case), "bf16", "no prefix")
