@@ -214,8 +214,10 @@ __global__ __launch_bounds__(256, GT == 4 ? 4 : 2) void decode_kernel(DecodePara
     const int nh = min(GT, p.group - hc * GT);
     const int npages = (ctx + bs - 1) >> p.bs_log2;
     cint32 *tbl = as_const(p.block_tables) + (size_t)b * p.max_blocks_per_seq;
-    const char *kpage_base = kbase + (size_t)g * head_stride + (size_t)chunk * 16;
-    const char *vpage_base = vbase + (size_t)g * head_stride + (size_t)chunk * 16;
+    // Wave-uniform bases; the per-lane part (slot row, 16-byte piece) is a
+    // 32-bit offset, so each load is a scalar page address plus one VGPR.
+    const char *kpage_base = kbase + (size_t)g * head_stride;
+    const char *vpage_base = vbase + (size_t)g * head_stride;
 
     // Query pieces of the GT heads (raw storage; exact).
     u32x4 q[GT];
@@ -244,14 +246,18 @@ __global__ __launch_bounds__(256, GT == 4 ? 4 : 2) void decode_kernel(DecodePara
     const int ntiles = ntiles_all > wave ? (ntiles_all - wave + kWaves - 1) / kWaves : 0;
     auto tile_start = [&](int t) { return start + (wave + t * kWaves) * TILE; };
 
-    // Block ids of the pages each load of a tile touches (wave-uniform).
+    // Tokens past the end of the partition are read as copies of its last
+    // token (same page, as pages hold a multiple of TPL tokens): their
+    // weight is exactly 0 and the copy is finite, so V needs no zeroing and
+    // the loads no branches.  Block ids of the pages each load of a tile
+    // touches (wave-uniform).
     auto fetch_ids = [&](int t, int *ids) {
       const int ts = tile_start(t);
 #pragma unroll
       for (int L = 0; L < NL; ++L) {
-        const int page = (ts + L * TPL) >> p.bs_log2;
+        const int page = min(ts + L * TPL, end - 1) >> p.bs_log2;
         int id = 0;
-        if (t < ntiles && page < npages) id = tbl[page];
+        if (t < ntiles) id = tbl[page];
         ids[L] = (int)min((unsigned)id, (unsigned)(p.num_blocks - 1));
       }
     };
@@ -259,16 +265,11 @@ __global__ __launch_bounds__(256, GT == 4 ? 4 : 2) void decode_kernel(DecodePara
       const int ts = tile_start(t);
 #pragma unroll
       for (int L = 0; L < NL; ++L) {
-        const int page = (ts + L * TPL) >> p.bs_log2;
-        if (page < npages) {
-          const int slot = (ts + L * TPL + tok) & (bs - 1);
-          const size_t off = (size_t)ids[L] * block_stride + (size_t)slot * G::kRowBytes;
-          kr[L] = ld16(kpage_base + off);
-          vr[L] = ld16(vpage_base + off);
-        } else {
-          kr[L] = u32x4{0u, 0u, 0u, 0u};
-          vr[L] = u32x4{0u, 0u, 0u, 0u};
-        }
+        const int slot = min(ts + L * TPL + tok, end - 1) & (bs - 1);
+        const size_t page_off = (size_t)ids[L] * block_stride;
+        const uint32_t lane_off = (uint32_t)(slot * G::kRowBytes + chunk * 16);
+        kr[L] = ld16(kpage_base + page_off + lane_off);
+        vr[L] = ld16(vpage_base + page_off + lane_off);
       }
     };
     const float c = p.scale_log2e;
@@ -313,10 +314,6 @@ __global__ __launch_bounds__(256, GT == 4 ? 4 : 2) void decode_kernel(DecodePara
       for (int L = 0; L < NL; ++L) {
         float vf[EPL];
         unpack16<E>(vr[L], vf);
-        if (tail && ts + L * TPL + tok >= end) {
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) vf[e] = 0.f;   // slots past the context may hold anything
-        }
 #pragma unroll
         for (int j = 0; j < GT; ++j)
 #pragma unroll
