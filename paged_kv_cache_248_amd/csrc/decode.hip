@@ -295,7 +295,7 @@ __global__ __launch_bounds__(256, GT == 4 ? 4 : 2) void decode_kernel(DecodePara
       for (int j = 0; j < GT; ++j) {
         float mx = x[j][0];
 #pragma unroll
-        for (int L = 1; L < NL; ++L) mx = fmaxf(mx, x[j][L]);
+        for (int L = 1; L < NL; ++L) mx = vmax(mx, x[j][L]);
         mx = uniformf(across_groups_max<LPT>(mx));
         if (mx > m[j]) {                     // wave-uniform branch
           const float alpha = fast_exp2(m[j] - mx);

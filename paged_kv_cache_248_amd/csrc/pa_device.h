@@ -113,13 +113,17 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// NaN-propagating maximum (IEEE maximum): lowers to v_maximum*_f32 without
+// the operand canonicalisation an IEEE fmax needs.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Max over lanes that differ only in the bits of STRIDE..32 (i.e. combine
 // the 64/STRIDE groups of STRIDE lanes).  STRIDE = 64 is a no-op.
 template <int STRIDE>
 __device__ __forceinline__ float across_groups_max(float v) {
-  if constexpr (STRIDE <= 8) v = fmaxf(v, dpp<kDppRor8>(v));
-  if constexpr (STRIDE <= 16) { const f32x2 r = pair_xor16(v); v = fmaxf(r[0], r[1]); }
-  if constexpr (STRIDE <= 32) { const f32x2 r = pair_xor32(v); v = fmaxf(r[0], r[1]); }
+  if constexpr (STRIDE <= 8) v = vmax(v, dpp<kDppRor8>(v));
+  if constexpr (STRIDE <= 16) { const f32x2 r = pair_xor16(v); v = vmax(r[0], r[1]); }
+  if constexpr (STRIDE <= 32) { const f32x2 r = pair_xor32(v); v = vmax(r[0], r[1]); }
   return v;
 }
 
