@@ -63,6 +63,26 @@ def test_decode_small_against_oracle(dtype, D, Hq, Hkv, bs):
         assert_close(host(out), ref, dtype, f"partition {part}")
 
 
+BLOCK_SIZES = [(dtype, D, bs) for dtype in ("f32", "f16", "bf16") for D in (64, 128)
+               for bs in (8, 64, 128, 256)]
+
+
+@pytest.mark.parametrize("dtype,D,bs", BLOCK_SIZES)
+def test_decode_block_sizes(dtype, D, bs):
+    """Pages of 8 tokens (a load's tokens fill one page exactly for fp32 rows)
+    and pages larger than a partition (64-token partitions inside 128/256-slot
+    pages); contexts ending mid-page and mid-tile."""
+    rng = np.random.default_rng(zlib.crc32(repr(("decode-bs", dtype, D, bs)).encode()))
+    ctx = np.concatenate([[1, bs - 1, bs + 3, 300], rng.integers(2, 900, size=2)])
+    log(f"decode block size dtype={dtype} D={D} bs={bs} ctx={ctx.tolist()}")
+    case = wl.make_decode(ctx, 8, 2, D, bs, dtype, seed=int(rng.integers(1 << 30)), device=DEV,
+                          poison=True)
+    ref = oracle_full(case)
+    for part in (-1, 64):
+        out = run_decode(case, partition_size=part)
+        assert_close(host(out), ref, dtype, f"block size {bs} partition {part}")
+
+
 def test_tiny_decode_f32_workload():
     case = wl.tiny_decode_f32(device=DEV, poison=True)
     log(f"tiny decode f32 ctx={case.kv.context_lens.tolist()}")
