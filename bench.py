@@ -270,8 +270,11 @@ def hbm_traffic(kernel_files, launches_key: str):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    # A GPU fresh from idle raises its shader clock over the first few
+    # hundred milliseconds of load; 300 untimed steps of each workload
+    # (0.1-0.4 s) let the timed steps run at the clock the kernel sustains.
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--only", default=None, choices=["llama7b_decode_f16", "gqa_decode_bf16",
                                                        "long_decode_f16", "prefill_bf16",
@@ -334,7 +337,7 @@ def main() -> int:
             torch.cuda.empty_cache()
         log("generating prefill_bf16 ...")
         pc = wl.prefill_bf16(device=dev)
-        r = bench_prefill(pa, torch, wl, pc, max(3, args.steps // 2), 2)
+        r = bench_prefill(pa, torch, wl, pc, args.steps, args.warmup)
         log(f"  prefill: {r['ms_per_step']:.3f} ms/step, {r['kernel_TFLOPs']:.0f} TFLOP/s")
         extra["prefill_bf16"] = r
         del pc

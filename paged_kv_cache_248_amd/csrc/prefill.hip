@@ -41,9 +41,13 @@
 //     the V^T operand is read with the transposing ds_read_b64_tr_b16; the
 //     operand reads of the next group of four MFMAs are in flight while the
 //     current four execute;
-//   * grid order is XCD-aware: the ids an XCD receives walk one (sequence,
-//     kv head) pair at a time through all its query tiles (the last, with the
-//     most keys, first), so the tiles sharing K/V run together in one L2.
+//   * the grid is persistent (one work-group per CU, each taking several
+//     work items), which removes the idle time between one work-group's end
+//     and the next one's start on a CU; the item order is XCD-aware: the
+//     work-groups of an XCD walk one (sequence, kv head) pair at a time
+//     through all its query tiles (the last, with the most keys, first), so
+//     the tiles sharing K/V run together in one L2.
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -221,23 +225,9 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
   const int col = lane & 31;      // query column owned by this lane
   const int half = lane >> 5;
 
-  // Work-group coordinates.  Work-group ids are dealt round-robin to the 8
-  // XCDs; id -> (xcd, local) -> (pair, query tile) makes each XCD run all the
-  // query tiles of one (sequence, kv head, head subgroup) pair together, so
-  // they stream the same K/V tiles through that XCD's L2 close in time.
-  int pair, qt;
-  {
-    const int n_qt = p.num_qtiles, n_pairs = p.num_pairs;
-    const int id = blockIdx.x;
-    const int xcd = id % kXcds, local = id / kXcds;
-    const int xcd_pairs = (n_pairs - xcd + kXcds - 1) / kXcds;   // pairs xcd, xcd+8, ...
-    if (local < xcd_pairs * n_qt) {
-      pair = xcd + kXcds * (local / n_qt);
-      qt = n_qt - 1 - local % n_qt;               // last query tile (most keys) first
-    } else {
-      return;                                     // padding of the grid to a multiple of 8
-    }
-  }
+  // One work item: the query tile qt of one (sequence, kv head, head
+  // subgroup) pair.
+  auto process = [&](const int pair, const int qt) {
   const int hs = pair % p.subgroups;
   const int g = (pair / p.subgroups) % p.num_kv_heads;
   const int b = pair / (p.subgroups * p.num_kv_heads);
@@ -599,6 +589,31 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
   };
   if (grp == 0) run(std::integral_constant<int, 0>{});
   else run(std::integral_constant<int, 1>{});
+  // Every wavefront's tile loads have landed (each waited for all of its
+  // own); the next item's prologue may refill any stage.
+  phase_sync();
+  };
+
+  // The grid is persistent: a multiple of 8 work-groups, at most one per
+  // CU.  Work-group ids are dealt round-robin to the 8 XCDs; XCD x owns the
+  // pairs x, x + 8, ...  and its work-groups take that list of items (pair
+  // by pair, the query tiles of a pair from the last, which has the most
+  // keys, to the first) in rounds of one item each, so that the query tiles
+  // of a pair run together and stream the same K/V tiles through that XCD's
+  // L2.  The order within a round alternates between rounds: a work-group
+  // that took one of the longer tiles of a pair takes one of the shorter
+  // ones of the next pair.
+  {
+    const int n_qt = p.num_qtiles;
+    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    const int per_xcd = gridDim.x / kXcds;
+    const int xcd_pairs = (p.num_pairs - xcd + kXcds - 1) / kXcds;
+    const int n_local = xcd_pairs * n_qt;
+    for (int r = 0; r * per_xcd < n_local; ++r) {
+      const int local = r * per_xcd + ((r & 1) ? per_xcd - 1 - slot : slot);
+      if (local < n_local) process(xcd + kXcds * (local / n_qt), n_qt - 1 - local % n_qt);
+    }
+  }
 }
 
 template <class E, int D>
@@ -627,9 +642,17 @@ hipError_t launch_typed(const PrefillLaunch &a, hipStream_t stream) {
   p.scale_log2e = a.scale * kLog2e;
   const long long pairs = (long long)a.num_seqs * a.num_kv_heads * p.subgroups;
   const long long qtiles = (a.max_query_len + p.pos_per_wg - 1) / p.pos_per_wg;
-  // each XCD gets ceil(pairs / 8) pairs' worth of slots
-  const long long grid = kXcds * ((pairs + kXcds - 1) / kXcds) * qtiles;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  // Items of the XCD with the most; one work-group per CU at most.
+  const long long xcd_items = ((pairs + kXcds - 1) / kXcds) * qtiles;
+  if (xcd_items > 0x7fffffffLL) return hipErrorInvalidValue;
+  int cus = 0;
+  {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+  }
+  const long long grid = kXcds * std::min<long long>(std::max(cus / kXcds, 1), xcd_items);
   p.num_pairs = (int32_t)pairs;
   p.num_qtiles = (int32_t)qtiles;
   const size_t lds_bytes = (size_t)2 * kStages * 64 * D * 2;
