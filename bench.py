@@ -121,7 +121,7 @@ def bench_decode(pa, torch, wl, case, steps, warmup):
         "block_size": kv.block_size, "dtype": case.dtype,
         "context_mean": float(ctx.mean()), "context_min": int(ctx.min()),
         "context_max": int(ctx.max()), "pool_blocks": int(kv.k_cache.shape[0]),
-        "partition_size": case.partition_size or pa.DEFAULT_PARTITION,
+        "partition_size": case.partition_size or pa.default_partition(Hq, Hkv),
     }
 
 

@@ -57,8 +57,12 @@ typedef enum {
 
 typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } pa_dtype_t;
 
-/* Library default KV partition length, in tokens, for split-KV decode. */
+/* Library default KV partition length, in tokens, for split-KV decode:
+ * PA_DEFAULT_PARTITION_GQA when num_heads / num_kv_heads >= 4 (each K/V
+ * tile then feeds several heads, and longer partitions halve the per-item
+ * overhead), else PA_DEFAULT_PARTITION. */
 #define PA_DEFAULT_PARTITION 512
+#define PA_DEFAULT_PARTITION_GQA 1024
 /* Most partitions one decode sequence may be split into
  * (ceil(min(max_context_len, max_blocks_per_seq*block_size) / partition)). */
 #define PA_MAX_PARTITIONS 2048
@@ -91,7 +95,7 @@ const char *pa_status_string(pa_status_t status);
  *                token's own K/V included), 1 <= context_lens[b] <= max_context_len
  *   max_context_len  host-side upper bound of context_lens (sizes the work)
  *   scale        softmax scale (normally 1/sqrt(head_dim))
- *   partition_size  tokens per split-KV partition: 0 = PA_DEFAULT_PARTITION,
+ *   partition_size  tokens per split-KV partition: 0 = the library default,
  *                a positive multiple of 64, or -1 = never split; at most
  *                PA_MAX_PARTITIONS partitions per sequence (else
  *                PA_ERR_UNSUPPORTED)

@@ -20,11 +20,17 @@ __all__ = [
     "paged_attn_decode", "paged_attn_decode_workspace_size",
     "paged_attn_prefill",
     "paged_kv_copy_blocks", "paged_kv_copy_blocks_workspace_size",
-    "DEFAULT_PARTITION",
+    "DEFAULT_PARTITION", "DEFAULT_PARTITION_GQA", "default_partition",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-DEFAULT_PARTITION = 512
+DEFAULT_PARTITION = 512       # PA_DEFAULT_PARTITION
+DEFAULT_PARTITION_GQA = 1024  # PA_DEFAULT_PARTITION_GQA
+
+
+def default_partition(num_heads: int, num_kv_heads: int) -> int:
+    """Partition length decode uses for partition_size=0 (same rule as the library)."""
+    return DEFAULT_PARTITION_GQA if num_heads // num_kv_heads >= 4 else DEFAULT_PARTITION
 
 _DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 

@@ -51,9 +51,10 @@ bool pow2_in(int32_t v, int32_t lo, int32_t hi) {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Partition length actually used (multiple of 64 tokens) and partition count.
-bool decode_partition(int32_t ctx_cap, int32_t partition_size, int32_t *part, int32_t *nparts) {
+bool decode_partition(int32_t ctx_cap, int32_t partition_size, int32_t group, int32_t *part,
+                      int32_t *nparts) {
   int64_t P;
-  if (partition_size == 0) P = PA_DEFAULT_PARTITION;
+  if (partition_size == 0) P = group >= 4 ? PA_DEFAULT_PARTITION_GQA : PA_DEFAULT_PARTITION;
   else if (partition_size == -1) P = std::max<int64_t>(64, ((int64_t)ctx_cap + 63) / 64 * 64);
   else if (partition_size > 0 && partition_size % 64 == 0) P = partition_size;
   else return false;
@@ -101,7 +102,9 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int
       max_context_len < 0)
     return 0;
   int32_t part = 0, nparts = 0;
-  if (!decode_partition(std::max(max_context_len, 1), partition_size, &part, &nparts)) return 0;
+  if (!decode_partition(std::max(max_context_len, 1), partition_size, num_heads / num_kv_heads,
+                        &part, &nparts))
+    return 0;
   return pa::decode_workspace_layout(num_seqs, num_heads, num_kv_heads, head_dim, nparts).total;
 }
 
@@ -125,7 +128,8 @@ pa_status_t paged_attn_decode(void *out, const void *query, const void *k_cache,
   const int32_t ctx_cap =
       (int32_t)std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * block_size);
   int32_t part = 0, nparts = 0;
-  if (!decode_partition(std::max(ctx_cap, 1), partition_size, &part, &nparts))
+  if (!decode_partition(std::max(ctx_cap, 1), partition_size, num_heads / num_kv_heads, &part,
+                        &nparts))
     return PA_ERR_UNSUPPORTED;
   if (nparts > PA_MAX_PARTITIONS) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0 || ctx_cap == 0) return PA_OK;

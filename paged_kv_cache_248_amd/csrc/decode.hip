@@ -393,6 +393,303 @@ __global__ __launch_bounds__(256, GT == 4 ? 4 : 2) void decode_kernel(DecodePara
   }
 }
 
+// ---- Matrix-core decode for grouped-query attention ----------------------
+// The GT query heads of a kv-head group (GT >= 4) share every K/V tile, so
+// the dot products are a small dense contraction per tile and run on the
+// matrix cores, which leaves the vector ALU only the softmax (about two
+// instructions per token instead of some twenty):
+//   S^T (16 tokens x 16 heads) = K (16 x D) Q^T (D x 16): D/32 MFMA
+//     16x16x32.  K goes from the cache straight into the operand layout
+//     (lane l: token l % 16, the 16 bytes at d = 32 ks + 8 (l / 16));
+//   O^T (D x 16 heads) += V^T (D x 16 tokens) P^T (16 tokens x 16 heads):
+//     D/16 MFMA 16x16x16.  V goes cache -> LDS by direct loads and is read
+//     back transposed (ds_read_b64_tr_b16).
+// Heads past the group are zero columns of Q^T.  The S^T accumulator gives
+// lane l head l % 16 for tokens 4 (l / 16) .. +3, which is exactly the P^T
+// operand layout of the PV step, so the softmax output feeds it directly.
+// Each wavefront keeps three tiles in flight (K in registers, V in its own
+// LDS stages) and waits for each with an exact vmcnt count.
+// 16-byte global load at sbase + voff + OFF, issued as inline assembly: the
+// compiler does not track it, so it inserts no wait of its own; the kernel
+// waits with an exact vmcnt and then ties the registers (tie_regs) before any
+// use.
+template <int OFF>
+__device__ __forceinline__ u32x4 gload16(const char *sbase, uint32_t voff) {
+  u32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3"
+               : "=v"(v) : "v"(voff), "s"(sbase), "i"(OFF) : "memory");
+  return v;
+}
+template <class E>
+__device__ __forceinline__ f32x4 mfma_k32(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
+  if constexpr (__is_same(typename E::storage, _Float16))
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <class E>
+__device__ __forceinline__ f32x4 mfma_k16(const u32x2 &a, const u32x2 &b, const f32x4 &c) {
+  if constexpr (__is_same(typename E::storage, _Float16))
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// Weights stay within [0, 2^kLazyDecode]: the running maximum is raised only
+// when a tile's maximum exceeds it by more than that.
+constexpr float kLazyDecode = 8.0f;
+
+template <class E, int D, int GT>
+__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeParams p) {
+  constexpr int T = 16;                  // tokens per tile
+  constexpr int KS = D / 32;             // QK k-steps
+  constexpr int DB = D / 16;             // PV d-blocks
+  constexpr int ROWB = D * 2;            // bytes of one token row
+  constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
+  constexpr int RPI = 1024 / ROWB;       // rows per direct-to-LDS instruction
+  constexpr int VI = T / RPI;            // direct-to-LDS instructions per V tile
+  constexpr int TILEB = T * ROWB;        // LDS bytes of one V tile
+  constexpr int NST = 3;                 // tiles in flight per wavefront
+  constexpr int PER_TILE = KS + VI;      // vector-memory operations per tile
+  static_assert(GT >= 4 && GT <= 16, "one 16-column MFMA block of heads");
+  static_assert(kWaves * GT * D * 4 <= kWaves * NST * TILEB, "partials fit the V stages");
+  __shared__ __attribute__((aligned(1024))) char s_v[kWaves * NST * TILEB];
+  __shared__ int s_item;
+  __shared__ float s_m[kWaves][GT], s_l[kWaves][GT];
+  float(*s_o)[GT][D] = reinterpret_cast<float(*)[GT][D]>(s_v);   // after the key loop
+
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid >> 6);
+  const int lane = tid & 63;
+  const int hl = lane & 15;         // head column of this lane
+  const int G = lane >> 4;          // token group: tokens 4G .. 4G+3 of a tile
+  const int bs = 1 << p.bs_log2;
+  const int Hq = p.num_heads, Hkv = p.num_kv_heads;
+  const size_t head_stride = (size_t)bs * ROWB;
+  const size_t block_stride = head_stride * (size_t)Hkv;
+  const int total = as_const(p.work_count)[0] * Hkv * p.head_chunks;
+
+  // V stages: row r of a tile holds its 16-byte chunk c at position
+  // c ^ vsw(r), vsw(r) = 2 (r mod 8) for 256-byte rows and 2 ((r / 2) mod 4)
+  // for 128-byte rows.  The transposing read of d-block db: lane l reads row
+  // l / 4, the 8 bytes at d = 16 db + 4 (l mod 4); the swizzle puts the 32
+  // lanes of each half-wave on distinct banks.  As the swizzle only moves
+  // 32-byte pairs, the address of d-block db is the d-block-0 address XOR 32 db.
+  auto vsw = [](int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); };
+  char *const my_v = s_v + wave * (NST * TILEB);
+  const uint32_t my_v_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)my_v;
+  uint32_t tr_addr[DB];
+  {
+    const int r = lane >> 2;
+    const uint32_t a0 = (uint32_t)(r * ROWB + 16 * vsw(r) + 8 * (lane & 3));
+#pragma unroll
+    for (int db = 0; db < DB; ++db) tr_addr[db] = my_v_addr + (a0 ^ (uint32_t)(32 * db));
+  }
+  // Direct-to-LDS lane mapping: instruction q, lane i fills row
+  // q RPI + i / CPR at chunk position i mod CPR, i.e. reads the row's global
+  // chunk (i mod CPR) ^ vsw(row).
+  int v_row[VI], v_chunk[VI];
+#pragma unroll
+  for (int q = 0; q < VI; ++q) {
+    v_row[q] = q * RPI + lane / CPR;
+    v_chunk[q] = ((lane % CPR) ^ vsw(v_row[q])) * 16;
+  }
+
+  for (;;) {
+    if (tid == 0) s_item = atomicAdd(p.next_item, 1);
+    __syncthreads();
+    const int item = s_item;
+    if (item >= total) break;
+    const int hc = item % p.head_chunks;
+    const int rest = item / p.head_chunks;
+    const int g = rest % Hkv;
+    const int wi = rest / Hkv;
+    const int b = as_const(p.work)[2 * wi];
+    const int part = as_const(p.work)[2 * wi + 1];
+    const int ctx = min(max(as_const(p.context_lens)[b], 0), p.ctx_cap);
+    const int start = part * p.partition;
+    const int end = min(start + p.partition, ctx);
+    const int nparts = (ctx + p.partition - 1) / p.partition;
+    const int h0 = g * p.group + hc * GT;
+    const int nh = min(GT, p.group - hc * GT);
+    cint32 *tbl = as_const(p.block_tables) + (size_t)b * p.max_blocks_per_seq;
+    const char *kpage_base = static_cast<const char *>(p.k_cache) + (size_t)g * head_stride;
+    const char *vpage_base = static_cast<const char *>(p.v_cache) + (size_t)g * head_stride;
+
+    // Q^T operand: lane l holds head h0 + l % 16, d = 32 ks + 8 (l / 16) .. +7.
+    u32x4 qf[KS];
+    {
+      const char *qp = static_cast<const char *>(p.query) +
+                       ((size_t)(b * Hq + h0 + hl) * D) * 2 + G * 16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = hl < nh ? ld16(qp + ks * 64) : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    // Tiles w, w + 4, ... of the partition.  Tiles start at multiples of 16
+    // tokens and pages hold at least 16, so a tile lies in one page; tokens
+    // past the partition end are read as copies of its last token (weight
+    // exactly 0, finite), so loads carry no branches.
+    const int ntiles_all = (end - start + T - 1) / T;
+    const int ntiles = ntiles_all > wave ? (ntiles_all - wave + kWaves - 1) / kWaves : 0;
+    auto tile_start = [&](int t) { return start + (wave + t * kWaves) * T; };
+    auto fetch_id = [&](int t) {
+      const int page = min(tile_start(t), end - 1) >> p.bs_log2;
+      int id = 0;
+      if (t < ntiles) id = tbl[page];
+      return (int)min((unsigned)id, (unsigned)(p.num_blocks - 1));
+    };
+    u32x4 kr[NST][KS];
+    auto issue = [&](int t, int id, auto buf_tag) {
+      constexpr int buf = decltype(buf_tag)::value;
+      const int ts = tile_start(t);
+      const size_t page_off = (size_t)id * block_stride;
+      const char *kp = kpage_base + page_off;
+      const char *vp = vpage_base + page_off;
+      const uint32_t koff = (uint32_t)((min(ts + hl, end - 1) & (bs - 1)) * ROWB + G * 16);
+      for_each_index(std::make_integer_sequence<int, KS>{}, [&](auto ks_tag) {
+        constexpr int ks = decltype(ks_tag)::value;
+        kr[buf][ks] = gload16<ks * 64>(kp, koff);
+      });
+#pragma unroll
+      for (int q = 0; q < VI; ++q) {
+        const uint32_t voff = (uint32_t)((min(ts + v_row[q], end - 1) & (bs - 1)) * ROWB + v_chunk[q]);
+        dma16(vp + voff, my_v + buf * TILEB + q * 1024);
+      }
+    };
+    // Tile loads still allowed in flight when tile t must have landed: the
+    // tiles issued after it (at most NST - 1; fewer near the end).
+    auto wait_tile = [&](int t) {
+      const int later = ntiles - 1 - t;
+      if (later >= 2) wait_vm<2 * PER_TILE>();
+      else if (later == 1) wait_vm<PER_TILE>();
+      else wait_vm<0>();
+    };
+
+    float m = -__builtin_inff(), l = 0.f;
+    f32x4 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float c = p.scale_log2e;
+    int id_next = 0;
+
+    auto step = [&](int t, auto buf_tag) {
+      constexpr int buf = decltype(buf_tag)::value;
+      constexpr int nbuf = (buf + 2) % NST;
+      // Tile t + 2 goes into the buffers tile t - 1 used (consumed last step).
+      if (t + 2 < ntiles) issue(t + 2, id_next, std::integral_constant<int, nbuf>{});
+      id_next = fetch_id(t + 3);
+      wait_tile(t);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(kr[buf][ks]));
+      u32x2 vt[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vt[db] = lds_tr16<buf * TILEB>(tr_addr[db]);
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sc = mfma_k32<E>(kr[buf][ks], qf[ks], sc);
+      // Softmax on S^T: lane (head l % 16) holds tokens ts + 4G + r, in log2
+      // units after scaling.
+      const int ts = tile_start(t);
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = sc[r] * c;
+      if (ts + T > end) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (ts + 4 * G + r >= end) x[r] = -__builtin_inff();
+      }
+      float mx = vmax(vmax(x[0], x[1]), vmax(x[2], x[3]));
+      const f32x2 m16 = pair_xor16(mx);
+      mx = vmax(m16[0], m16[1]);
+      const f32x2 m32 = pair_xor32(mx);
+      mx = vmax(m32[0], m32[1]);
+      if (__any(mx > m + kLazyDecode)) {
+        const float m_new = vmax(m, mx);
+        const float alpha = fast_exp2(m - m_new);        // 0 when m was -inf
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        m = m_new;
+      }
+      float e[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) e[r] = fast_exp2(x[r] - m);
+      l += (e[0] + e[1]) + (e[2] + e[3]);
+      const u32x2 pt = {pack2<E>(e[0], e[1]), pack2<E>(e[2], e[3])};
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(vt[0]), "+v"(vt[DB - 1]));
+#pragma unroll
+      for (int db = 1; db < DB - 1; ++db) asm volatile("" : "+v"(vt[db]));
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = mfma_k16<E>(vt[db], pt, o[db]);
+    };
+
+    if (ntiles > 0) {
+      issue(0, fetch_id(0), std::integral_constant<int, 0>{});
+      if (ntiles > 1) issue(1, fetch_id(1), std::integral_constant<int, 1>{});
+      id_next = fetch_id(2);
+      // Q, the first two tiles and whatever the previous work item stored
+      // (stores and loads do not complete in one order, so the exact counts
+      // below start from an empty queue).
+      wait_vm<0>();
+      for (int t = 0; t < ntiles; t += NST) {
+        step(t, std::integral_constant<int, 0>{});
+        if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
+        if (t + 2 < ntiles) step(t + 2, std::integral_constant<int, 2>{});
+      }
+    }
+
+    // L of a head is spread over the four token groups; O^T is complete.
+    {
+      const f32x2 a = pair_xor16(l);
+      const float l2 = a[0] + a[1];
+      const f32x2 b2 = pair_xor32(l2);
+      l = b2[0] + b2[1];
+    }
+    __syncthreads();          // every wavefront is done with its V stages
+    if (hl < nh) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<f32x4 *>(&s_o[wave][hl][16 * db + 4 * G]) = o[db];
+      if (G == 0) {
+        s_m[wave][hl] = m;
+        s_l[wave][hl] = l;
+      }
+    }
+    __syncthreads();
+
+    for (int idx = tid; idx < GT * D; idx += 256) {
+      const int j = idx / D, d = idx % D;
+      if (j >= nh) continue;
+      float M = s_m[0][j];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][j]);
+      float L = 0.f, O = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float cw = fast_exp2(s_m[w][j] - M);     // idle waves: 2^-inf = 0
+        L = fmaf(cw, s_l[w][j], L);
+        O = fmaf(cw, s_o[w][j][d], O);
+      }
+      const size_t row = (size_t)(b * Hq + h0 + j);
+      if (nparts <= 1) {
+        store_elem<E>(p.out, row * D + d, O / L);
+      } else {
+        const size_t slot = row * p.max_parts + part;
+        p.part_o[slot * D + d] = O;
+        if (d == 0) {
+          p.part_ml[slot * 2] = M;
+          p.part_ml[slot * 2 + 1] = L;
+        }
+      }
+    }
+    __syncthreads();   // LDS and s_item are reused by the next item
+  }
+}
+
 // Builds the compact list of (sequence, partition) work items — full-length
 // partitions first, each sequence's shorter last partition after them — and
 // clears the dynamic work counter.
@@ -521,7 +818,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(void *out, const floa
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-template <class E, int D, int GT>
+template <class E, int D, int GT, bool MF>
 hipError_t launch_typed(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStream_t stream) {
   char *w = static_cast<char *>(a.workspace);
   DecodeParams p;
@@ -556,21 +853,23 @@ hipError_t launch_typed(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStr
 
   // Resident work-groups per CU; items are fetched dynamically, so a grid
   // larger than what fits only queues (it cannot unbalance the work).
-  static int occ_cache[3][2][4] = {};
-  const int ti = (int)a.dtype, di = D == 128, gi = GT == 1 ? 0 : GT == 2 ? 1 : GT == 4 ? 2 : 3;
-  int occ = occ_cache[ti][di][gi];
+  auto kernel = [] {
+    if constexpr (MF) return decode_mfma_kernel<E, D, GT>;
+    else return decode_kernel<E, D, GT>;
+  }();
+  static int occ = 0;   // per instantiation
   if (occ == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_kernel<E, D, GT>, 256, 0) !=
-            hipSuccess || occ < 1)
-      occ = 2;
-    occ_cache[ti][di][gi] = occ;
+    int o = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kernel, 256, 0) != hipSuccess || o < 1)
+      o = 2;
+    occ = o;
   }
   const long long upper =
       (long long)a.num_seqs * a.max_parts * a.num_kv_heads * p.head_chunks;
   const long long resident = (long long)device_cu_count() * occ;
   const int grid = (int)std::max(1LL, std::min(upper, resident));
   profile_begin(stream);
-  hipLaunchKernelGGL((decode_kernel<E, D, GT>), dim3(grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, stream, p);
   profile_end(stream);
   if (a.max_parts > 1) {
     hipLaunchKernelGGL((decode_merge_kernel<E, D, GT>),
@@ -585,10 +884,20 @@ hipError_t launch_typed(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStr
 template <class E, int D>
 hipError_t launch_group(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStream_t s) {
   const int group = a.num_heads / a.num_kv_heads;
-  if (group == 1) return launch_typed<E, D, 1>(a, ws, s);
-  if (group == 2) return launch_typed<E, D, 2>(a, ws, s);
-  if (group <= 4) return launch_typed<E, D, 4>(a, ws, s);
-  return launch_typed<E, D, 8>(a, ws, s);
+  // 16-bit caches with a group of 4 or more heads per kv head and pages of
+  // at least 16 tokens take the matrix-core kernel (one 16-column block of
+  // heads per work item).
+  if constexpr (E::bytes == 2) {
+    if (group >= 4 && a.block_size >= 16) {
+      if (group == 4) return launch_typed<E, D, 4, true>(a, ws, s);
+      if (group <= 8) return launch_typed<E, D, 8, true>(a, ws, s);
+      return launch_typed<E, D, 16, true>(a, ws, s);
+    }
+  }
+  if (group == 1) return launch_typed<E, D, 1, false>(a, ws, s);
+  if (group == 2) return launch_typed<E, D, 2, false>(a, ws, s);
+  if (group <= 4) return launch_typed<E, D, 4, false>(a, ws, s);
+  return launch_typed<E, D, 8, false>(a, ws, s);
 }
 
 template <class E>

@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
+#include <utility>
 #include <stdint.h>
 
 namespace pa {
@@ -11,6 +13,8 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -137,5 +141,53 @@ __device__ __forceinline__ float across_groups_sum(float v) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- Explicit memory pipelining ------------------------------------------
+// s_waitcnt vmcnt(N): at most N vector-memory operations of this wavefront
+// still outstanding (loads complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One direct-to-LDS load of 1 KB: lane i's 16 bytes at src land at dst + 16 i
+// (dst is the same for the whole wavefront).
+__device__ __forceinline__ void dma16(const void *src, char *dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+}
+
+// MFMA operand reads from LDS, issued as inline assembly: the compiler does
+// not associate them with the direct-to-LDS loads (whose completion the
+// kernels await themselves), keeps them in program order with the other
+// volatile statements, and leaves their completion to an explicit lgkmcnt
+// wait.  Addresses are LDS byte addresses.
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_b128(uint32_t addr) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+  return v;
+}
+// Transposing read (ds_read_b64_tr_b16): in each group of 16 lanes, lane i
+// receives element j from lane 4j + i/4, element i mod 4 of that lane's 8 bytes.
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_tr16(uint32_t addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+  return v;
+}
+
+// Calls f(integral_constant<int, i>) for i = 0, 1, ... in order.
+template <int... is, class F>
+__device__ __forceinline__ void for_each_index(std::integer_sequence<int, is...>, F &&f) {
+  (f(std::integral_constant<int, is>{}), ...);
+}
+
+// Two fp32 values -> the element type's packed pair (round to nearest even).
+template <class E>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (__is_same(typename E::storage, _Float16)) return pack_f16(a, b);
+  else return pack_bf16(a, b);
+}
 
 }  // namespace pa

@@ -89,11 +89,6 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <class E>
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  if constexpr (__is_same(typename E::storage, _Float16)) return pack_f16(a, b);
-  else return pack_bf16(a, b);
-}
 
 // V^T tile layout.  Row d holds the tile's 64 keys; inside every group of 16
 // keys the key order is k -> (k & 3) | bit3(k) << 2 | bit2(k) << 3, which puts
@@ -146,38 +141,6 @@ __device__ __forceinline__ void phase_sync() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// s_waitcnt vmcnt(N): at most N vector-memory operations of this wavefront
-// still outstanding (they complete in issue order).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// One direct-to-LDS load of 1 KB: lane i's 16 bytes at src land at dst + 16 i.
-__device__ __forceinline__ void dma16(const void *src, char *dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
-}
-
-// MFMA operand reads from LDS, issued as inline assembly: the compiler does
-// not associate them with the direct-to-LDS loads (whose completion the
-// kernel awaits itself), keeps them in program order with the other volatile
-// statements, and leaves their completion to lds_tie.  Addresses are LDS
-// byte addresses.
-template <int OFF>
-__device__ __forceinline__ u32x4 lds_b128(uint32_t addr) {
-  u32x4 v;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
-  return v;
-}
-// Transposing read (ds_read_b64_tr_b16): in each group of 16 lanes, lane i
-// receives element j from lane 4j + i/4, element i mod 4 of that lane's 8 bytes.
-template <int OFF>
-__device__ __forceinline__ u32x2 lds_tr16(uint32_t addr) {
-  u32x2 v;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
-  return v;
-}
 // s_waitcnt lgkmcnt(N), tied to the registers it makes valid so that their
 // users stay after it.
 template <int N>
@@ -185,11 +148,6 @@ __device__ __forceinline__ void lds_tie(u32x4 (&r)[4]) {
   asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) : "i"(N));
 }
 
-// Calls f(integral_constant<int, i>) for i = 0, 1, ... in order.
-template <int... is, class F>
-__device__ __forceinline__ void for_each_index(std::integer_sequence<int, is...>, F &&f) {
-  (f(std::integral_constant<int, is>{}), ...);
-}
 
 // Scalar load of base[idx] (idx uniform), issued where it stands; its value
 // may be used only after sload_tie.  Block-table entries are read this way so

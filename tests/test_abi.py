@@ -109,6 +109,19 @@ def test_decode_workspace_size(lib):
     assert lib.paged_attn_decode_workspace_size(4, 8, 2, 128, 4096, -1) == small
 
 
+def test_decode_default_partition_depends_on_group(lib):
+    """partition_size 0 picks 1024 tokens for 4+ heads per kv head, else 512."""
+    import paged_kv_cache_248_amd as pa
+    ws = lib.paged_attn_decode_workspace_size
+    # group 4 (8 heads, 2 kv heads)
+    assert ws(4, 8, 2, 128, 4096, 0) == ws(4, 8, 2, 128, 4096, 1024) != ws(4, 8, 2, 128, 4096, 512)
+    # group 2 and MHA
+    assert ws(4, 8, 4, 128, 4096, 0) == ws(4, 8, 4, 128, 4096, 512) != ws(4, 8, 4, 128, 4096, 1024)
+    assert ws(4, 8, 8, 128, 4096, 0) == ws(4, 8, 8, 128, 4096, 512)
+    assert pa.default_partition(8, 2) == 1024 and pa.default_partition(8, 4) == 512
+    assert pa.default_partition(32, 32) == pa.DEFAULT_PARTITION == 512
+
+
 def _prefill(lib, **kw):
     a = dict(out=P, query=P, k=P, v=P, bt=P, cl=P, qsl=P2, B=2, T=10, maxq=8, maxctx=40, Hq=8,
              Hkv=2, D=128, bs=16, nblk=64, mbps=8, scale=0.125, dtype=2, stream=None)

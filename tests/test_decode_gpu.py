@@ -83,6 +83,25 @@ def test_decode_block_sizes(dtype, D, bs):
         assert_close(host(out), ref, dtype, f"block size {bs} partition {part}")
 
 
+LARGE_GROUPS = [(dtype, D, Hq) for dtype in ("f16", "bf16") for D in (64, 128)
+                for Hq in (32, 40, 64)]
+
+
+@pytest.mark.parametrize("dtype,D,Hq", LARGE_GROUPS)
+def test_decode_large_groups(dtype, D, Hq):
+    """16, 20 and 32 query heads per kv head: one full block of 16 heads, a
+    full block plus a 4-head block, and two full blocks per work item chunk."""
+    rng = np.random.default_rng(zlib.crc32(repr(("decode-groups", dtype, D, Hq)).encode()))
+    ctx = np.concatenate([[1, 16, 17, 1000], rng.integers(2, 1500, size=2)])
+    log(f"decode large group dtype={dtype} D={D} Hq={Hq} Hkv=2 ctx={ctx.tolist()}")
+    case = wl.make_decode(ctx, Hq, 2, D, 16, dtype, seed=int(rng.integers(1 << 30)), device=DEV,
+                          poison=True)
+    ref = oracle_full(case)
+    for part in (-1, 0, 128):
+        out = run_decode(case, partition_size=part)
+        assert_close(host(out), ref, dtype, f"group {Hq // 2} partition {part}")
+
+
 def test_tiny_decode_f32_workload():
     case = wl.tiny_decode_f32(device=DEV, poison=True)
     log(f"tiny decode f32 ctx={case.kv.context_lens.tolist()}")
