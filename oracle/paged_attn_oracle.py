@@ -27,6 +27,11 @@ Readings of points the pages leave open (all also listed in the design notes):
   * prefill: context_lens[b] counts prefix + new keys; new query t of a
     sequence with q_b new tokens sits at absolute position
     context_lens[b] - q_b + t and sees keys 0..position (bottom-right causal);
+  * KV append: context_lens[b] counts the cached tokens after the append
+    (as for prefill), so new token i of a sequence with q_b new tokens is
+    logical token context_lens[b] - q_b + i; a token whose position is
+    negative or past its table row, or whose table entry is not a block of
+    the pool, is not written;
   * block copy: src_to_dst[i] = j copies source block i into destination
     block j; when several i name the same j the lowest i is the one taken, and
     it is taken only if it is a valid source index; -1 and any j outside the
@@ -50,6 +55,7 @@ __all__ = [
     "split_merge_ref",
     "decode_split_ref",
     "copy_blocks_ref",
+    "append_kv_ref",
 ]
 
 
@@ -249,4 +255,40 @@ def copy_blocks_ref(src: np.ndarray, dst: np.ndarray, src_to_dst) -> np.ndarray:
     sb = src.reshape(num_src, -1).view(np.uint8)
     ob = out.reshape(num_dst, -1).view(np.uint8)
     ob[vals[take]] = sb[first[take]]
+    return out
+
+
+def append_kv_ref(cache: np.ndarray, new_rows: np.ndarray, block_tables, context_lens,
+                  query_start_loc) -> np.ndarray:
+    """Write new tokens' K (or V) rows into the paged pool; returns the new pool.
+
+    [P-opt] PagedAttention section, the PagedKVCache sketch: ``append`` adds a
+    sequence's new KV rows after its cached ones, taking pool blocks through
+    the sequence's block table; [P-wall] §二.2: logical token j of a sequence
+    lives in physical block block_table[j // block_size] at row
+    j % block_size.  new_rows is [total_new_tokens, kv_heads, head_dim]; the
+    new tokens of sequence b are rows query_start_loc[b] ..
+    query_start_loc[b + 1] - 1, and token i of them is logical token
+    context_lens[b] - q_b + i.  Tokens are written one by one in (sequence,
+    token) order, every kv head of a token at once, byte for byte; a token
+    with no valid destination is skipped.  Callers run this once for the K
+    pool and once for the V pool.
+    """
+    out = np.array(cache, copy=True)
+    num_blocks, _, block_size, _ = out.shape
+    tables = np.asarray(block_tables)
+    ctx = np.asarray(context_lens).astype(np.int64)
+    qsl = np.asarray(query_start_loc).astype(np.int64)
+    rows = np.asarray(new_rows)
+    max_pos = tables.shape[1] * block_size
+    for b in range(len(ctx)):
+        q_b = int(qsl[b + 1] - qsl[b])
+        for i in range(q_b):
+            pos = int(ctx[b]) - q_b + i
+            if pos < 0 or pos >= max_pos:
+                continue
+            blk = int(tables[b, pos // block_size])
+            if blk < 0 or blk >= num_blocks:
+                continue
+            out[blk, :, pos % block_size, :] = rows[qsl[b] + i]
     return out

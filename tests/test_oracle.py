@@ -11,8 +11,9 @@ import pytest
 import torch
 
 import workloads as wl
-from oracle import (attend_two_pass, copy_blocks_ref, decode_ref, decode_split_ref,
-                    gather_sequence, online_softmax_ref, prefill_ref, split_merge_ref)
+from oracle import (append_kv_ref, attend_two_pass, copy_blocks_ref, decode_ref,
+                    decode_split_ref, gather_sequence, online_softmax_ref, prefill_ref,
+                    split_merge_ref)
 
 
 def _np(t):
@@ -375,3 +376,107 @@ def test_prefill_flop_model_small():
     # ctx 5 with 3 new tokens: rows see 3, 4, 5 keys -> 12 pairs
     assert wl.prefill_pairs([5], [3]) == 12
     assert wl.prefill_flops([5], [3], 2, 4) == 4 * 4 * 2 * 12
+
+
+# ---------------------------------------------------------------- KV append
+def _append_example_arrays(g, D=3):
+    names = ["req_A", "req_B"]
+    tables = [g["block_tables"][n] for n in names]
+    bt = np.full((2, 3), -1, dtype=np.int32)
+    for i, t in enumerate(tables):
+        bt[i, :len(t)] = t
+    cl = np.array([g["context_lens"][n] for n in names], dtype=np.int32)
+    qsl = np.array([0, cl[0], cl[0] + cl[1]], dtype=np.int32)      # every token is new
+    rows = (np.arange(int(qsl[-1]))[:, None, None] + 1 + np.zeros((1, 1, D))).astype(np.float32)
+    pool = np.full((g["num_blocks"], 1, g["block_size"], D), -7.0, dtype=np.float32)
+    return names, bt, cl, qsl, rows, pool
+
+
+def test_append_block_manager_example(golden_dir):
+    """The page's allocator run (req_A: 20 + 13 tokens over blocks [0, 1, 3];
+    req_B: 10 tokens in block 2): each token lands in the block and row the
+    allocation implies, and nothing else changes."""
+    g = json.load(open(os.path.join(golden_dir, "append_block_manager_example.json")))
+    names, bt, cl, qsl, rows, pool = _append_example_arrays(g)
+    out = append_kv_ref(pool, rows, bt, cl, qsl)
+    for name, tok, blk, row in g["expected_slots"]:
+        r = int(qsl[names.index(name)]) + tok
+        assert np.array_equal(out[blk, 0, row], rows[r, 0]), (name, tok)
+    for blk in g["untouched_blocks"]:
+        assert np.array_equal(out[blk], pool[blk])
+    for blk, row in g["untouched_rows"]:
+        assert np.array_equal(out[blk, 0, row], pool[blk, 0, row])
+    assert int((out != pool).any(axis=(1, 3)).sum()) == int(cl.sum())
+
+
+def test_append_then_gather_returns_the_rows():
+    """New tokens appended after a cached prefix read back, through the block
+    table, at positions context_len - q_b .. context_len - 1; the prefix and
+    every other slot keep their bytes."""
+    rng = np.random.default_rng(11)
+    bs, Hkv, D, nb = 4, 2, 5, 40
+    ctx = np.array([7, 4, 13, 1])
+    q = np.array([3, 4, 5, 1])
+    qsl = np.concatenate([[0], np.cumsum(q)]).astype(np.int32)
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = perm[:16].reshape(4, 4)
+    pool = rng.integers(0, 2**16, size=(nb, Hkv, bs, D), dtype=np.uint16)
+    rows = rng.integers(0, 2**16, size=(int(qsl[-1]), Hkv, D), dtype=np.uint16)
+    out = append_kv_ref(pool, rows, bt, ctx, qsl)
+    for b in range(4):
+        for h in range(Hkv):
+            got = gather_sequence(out, bt[b], int(ctx[b]), h)
+            old = gather_sequence(pool, bt[b], int(ctx[b]), h)
+            n_old = int(ctx[b] - q[b])
+            assert np.array_equal(got[:n_old], old[:n_old])
+            assert np.array_equal(got[n_old:], rows[qsl[b]:qsl[b + 1], h])
+    used = set()
+    for b in range(4):
+        for j in range(int(ctx[b] - q[b]), int(ctx[b])):
+            used.add((int(bt[b, j // bs]), j % bs))
+    for blk in range(nb):
+        for r in range(bs):
+            if (blk, r) not in used:
+                assert np.array_equal(out[blk, :, r], pool[blk, :, r])
+
+
+def test_append_in_two_calls_equals_one_call():
+    """Appending a sequence's new tokens in two calls (context_lens counting
+    the tokens present after each) leaves the same pool as one call."""
+    rng = np.random.default_rng(12)
+    bs, nb = 8, 12
+    pool = rng.normal(size=(nb, 2, bs, 4)).astype(np.float32)
+    bt = rng.permutation(nb)[:6].astype(np.int32).reshape(2, 3)
+    ctx = np.array([20, 17])
+    q = np.array([9, 17])
+    rows = rng.normal(size=(int(q.sum()), 2, 4)).astype(np.float32)
+    one = append_kv_ref(pool, rows, bt, ctx, np.array([0, 9, 26]))
+    # first call: 4 and 10 of the new tokens; second call: the rest
+    first = np.concatenate([rows[0:4], rows[9:19]])
+    second = np.concatenate([rows[4:9], rows[19:26]])
+    two = append_kv_ref(pool, first, bt, ctx - np.array([5, 7]), np.array([0, 4, 14]))
+    two = append_kv_ref(two, second, bt, ctx, np.array([0, 5, 12]))
+    assert np.array_equal(one, two)
+
+
+def test_append_skips_tokens_without_a_destination():
+    """Positions before 0 (more new tokens than the context holds), past the
+    table row, and table entries that are not pool blocks are not written."""
+    bs, nb = 4, 6
+    pool = np.zeros((nb, 1, bs, 2), dtype=np.float32)
+    bt = np.array([[0, 1], [-1, 2], [3, 99]], dtype=np.int32)
+    ctx = np.array([2, 8, 8])                     # seq 0: 3 new tokens but 2 in context
+    q = np.array([3, 8, 8])
+    qsl = np.concatenate([[0], np.cumsum(q)])
+    rows = (np.arange(int(qsl[-1]), dtype=np.float32)[:, None, None] + 1) * np.ones((1, 1, 2))
+    out = append_kv_ref(pool, rows, bt, ctx, qsl)
+    assert np.array_equal(out[0, 0, 0], rows[1, 0]) and np.array_equal(out[0, 0, 1], rows[2, 0])
+    assert np.array_equal(out[2, 0], rows[7:11, 0])      # seq 1, positions 4..7; 0..3 skipped
+    assert np.array_equal(out[3, 0], rows[11:15, 0])     # seq 2, positions 0..3; 4..7 skipped
+    for blk in (1, 4, 5):
+        assert not out[blk].any()
+    # positions past the table row (2 blocks of 4) are skipped as well
+    out2 = append_kv_ref(pool, rows[:3], bt[:1], np.array([11]), np.array([0, 3]))   # 8, 9, 10
+    assert not out2.any()
+    out3 = append_kv_ref(pool, rows[:3], bt[:1], np.array([10]), np.array([0, 3]))   # 7 fits
+    assert np.array_equal(out3[1, 0, 3], rows[0, 0]) and int((out3 != 0).any(axis=3).sum()) == 1

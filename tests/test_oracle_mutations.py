@@ -88,6 +88,22 @@ def _decode_mod_group(query, k_cache, v_cache, block_tables, context_lens, scale
     return out
 
 
+_orig_append = O.append_kv_ref
+
+
+def _append_off_by_one(cache, rows, block_tables, context_lens, qsl):
+    # wrong position: token i of a sequence written one slot later
+    return _orig_append(cache, rows, block_tables, np.asarray(context_lens) + 1, qsl)
+
+
+def _append_ignores_table(cache, rows, block_tables, context_lens, qsl):
+    # wrong index: logical block number used as the physical block
+    nb, _, bs, _ = np.asarray(cache).shape
+    ident = np.tile(np.arange(np.asarray(block_tables).shape[1], dtype=np.int64),
+                    (len(context_lens), 1))
+    return _orig_append(cache, rows, ident, context_lens, qsl)
+
+
 MUTANTS = [
     ("gather ignores block table", O, "gather_sequence", _gather_ignores_table,
      [lambda: [pins.test_decode_matches_brute_force(bs) for bs in (1, 2, 16)]]),
@@ -106,7 +122,17 @@ MUTANTS = [
      [pins.test_prefill_single_new_token_equals_decode]),
     ("gqa map h % Hkv", pins, "decode_ref", _decode_mod_group,
      [pins.test_gqa_equals_mha_on_repeated_kv]),
+    ("append position off by one", pins, "append_kv_ref", _append_off_by_one,
+     [lambda: pins.test_append_block_manager_example(pins_golden())]),
+    ("append ignores block table", pins, "append_kv_ref", _append_ignores_table,
+     [lambda: pins.test_append_block_manager_example(pins_golden()),
+      pins.test_append_then_gather_returns_the_rows]),
 ]
+
+
+def pins_golden():
+    import os
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
 @pytest.mark.parametrize("name,mod,attr,fn,checks", MUTANTS, ids=[m[0] for m in MUTANTS])
