@@ -6,7 +6,7 @@ the LLaMA-7B-shaped decode workload: 64 sequences, 32 heads, head_dim 128,
 block_size 16, contexts uniform in [512, 4096], fp16, inputs resident in HBM.
 The headline value is its algorithmic KV bandwidth (GB/s).  The same run also
 measures the GQA bf16 and long-context split-KV decode workloads, the causal
-paged prefill (TFLOP/s) and the block copy (GB/s), and times the fp64 CPU
+paged prefill (TFLOP/s), the block copy and the KV append (GB/s), and times the fp64 CPU
 oracle on a bounded sample of the headline workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
@@ -178,6 +178,30 @@ def bench_copy(pa, torch, wl, case, steps, warmup):
     }
 
 
+def bench_append(pa, torch, wl, case, steps, warmup):
+    kv = case.kv
+    T, Hkv, D = case.key.shape
+    # Rows (64 MiB) and touched pool slots fit the 256 MB Infinity Cache:
+    # overwrite a 1 GiB scratch buffer between steps so every step starts cold.
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=case.key.device)
+
+    def step():
+        pa.paged_kv_append(kv.k_cache, kv.v_cache, case.key, case.value, kv.block_tables,
+                           kv.context_lens, case.query_start_loc)
+
+    timer = KernelTimer(pa, torch, steps)
+    ms = timed_steps(torch, step, steps, warmup, timer, between=lambda: scratch.fill_(1))
+    kms = timer.mean_ms()
+    nbytes = wl.append_bytes(T, kv.context_lens.numel(), Hkv, D, kv.block_size,
+                             wl.ELEM_BYTES[case.dtype])
+    return {
+        "workload": case.name, "kernel_ms": kms, "bytes": nbytes, "new_tokens": T,
+        "kernel_GBps": nbytes / (kms * 1e-3) / 1e9,
+        "frac_hbm_peak": nbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "step_ms_incl_cache_flush": ms,
+    }
+
+
 def bench_stream_copy(torch, steps, warmup, nbytes: int = 2 << 30):
     """A plain device-to-device copy of known size: the practical HBM ceiling
     for a read+write stream, and the reference that scales the FETCH_SIZE /
@@ -278,7 +302,7 @@ def main() -> int:
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--only", default=None, choices=["llama7b_decode_f16", "gqa_decode_bf16",
                                                        "long_decode_f16", "prefill_bf16",
-                                                       "copy_bf16", "stream_copy"],
+                                                       "copy_bf16", "append_bf16", "stream_copy"],
                     help="run one workload, print its result object and exit (profiling)")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
@@ -313,6 +337,8 @@ def main() -> int:
             r = bench_prefill(pa, torch, wl, case, args.steps, args.warmup)
         elif args.only.startswith("copy"):
             r = bench_copy(pa, torch, wl, case, args.steps, args.warmup)
+        elif args.only.startswith("append"):
+            r = bench_append(pa, torch, wl, case, args.steps, args.warmup)
         else:
             r = bench_decode(pa, torch, wl, case, args.steps, args.warmup)
         print(json.dumps(r), flush=True)
@@ -347,6 +373,13 @@ def main() -> int:
         log(f"  copy: {r['kernel_ms']:.3f} ms, {r['kernel_GBps']:.0f} GB/s")
         extra["copy_bf16"] = r
         del cc
+        torch.cuda.empty_cache()
+        log("generating append_bf16 ...")
+        ac = wl.append_bf16(device=dev)
+        r = bench_append(pa, torch, wl, ac, args.steps, args.warmup)
+        log(f"  append: {r['kernel_ms']:.4f} ms, {r['kernel_GBps']:.0f} GB/s")
+        extra["append_bf16"] = r
+        del ac
         torch.cuda.empty_cache()
 
     cpu = None

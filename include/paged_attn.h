@@ -192,13 +192,50 @@ pa_status_t paged_kv_copy_blocks(const void *src_k, const void *src_v, void *dst
                                  void *stream);
 
 /* --------------------------------------------------------------------------
+ * Paged KV append: write the K and V rows of newly computed tokens into the
+ * slots their block tables give them ([P-opt], the PagedKVCache sketch of the
+ * PagedAttention section: append adds a sequence's new KV rows after its
+ * cached ones through its block table; [P-wall] §二.2: logical token j lives
+ * in block block_tables[b][j / block_size] at row j % block_size).
+ *
+ *   k_cache, v_cache  [num_blocks, num_kv_heads, block_size, head_dim]
+ *                 pools, written in place; v_cache and value may both be
+ *                 NULL to append K only
+ *   key, value    [total_tokens, num_kv_heads, head_dim] rows of the new
+ *                 tokens, packed by sequence: sequence b owns rows
+ *                 query_start_loc[b] .. query_start_loc[b + 1] - 1
+ *   block_tables  [num_seqs, max_blocks_per_seq] int32, entries for every
+ *                 block the new tokens reach already allocated
+ *   context_lens  [num_seqs] int32, tokens cached AFTER the append (prefix +
+ *                 new, as for paged_attn_prefill): new token i of sequence b,
+ *                 with q_b new tokens, is logical token context_lens[b] - q_b + i
+ *   query_start_loc  [num_seqs + 1] int32, non-decreasing from 0 to
+ *                 total_tokens
+ *   head_dim      head_dim * element bytes a multiple of 16; block_size a
+ *                 power of two in [8, 256]; every pool and row pointer
+ *                 16-byte aligned
+ *
+ * Bytes are copied unchanged.  A token whose position is negative or at or
+ * past max_blocks_per_seq * block_size, or whose table entry is outside
+ * [0, num_blocks), is skipped; no other slot is written.  Two new tokens that
+ * name the same slot leave either one's row there.  The call is asynchronous
+ * on `stream`; total_tokens == 0 or num_seqs == 0 launches nothing.
+ * ------------------------------------------------------------------------ */
+pa_status_t paged_kv_append(void *k_cache, void *v_cache, const void *key, const void *value,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            const int32_t *query_start_loc, int32_t num_seqs,
+                            int32_t total_tokens, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                            pa_dtype_t dtype, void *stream);
+
+/* --------------------------------------------------------------------------
  * Measurement hook.
  *
  * With non-NULL events (hipEvent_t passed as void*, created by the caller),
  * every later call records `start` on its stream just before its main kernel
  * (decode: the attention kernel; prefill: the attention kernel; copy: the copy
- * kernel) and `stop` just after it, so the caller can read that kernel's
- * duration with hipEventElapsedTime.  Pass NULL, NULL to stop recording.  The
+ * kernel; append: the append kernel) and `stop` just after it, so the caller
+ * can read that kernel's duration with hipEventElapsedTime.  Pass NULL, NULL to stop recording.  The
  * setting is process-wide and not synchronised: set it from the thread that
  * issues the calls being measured.  Returns PA_ERR_NULL if exactly one event
  * is NULL.

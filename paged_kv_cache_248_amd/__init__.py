@@ -20,6 +20,7 @@ __all__ = [
     "paged_attn_decode", "paged_attn_decode_workspace_size",
     "paged_attn_prefill",
     "paged_kv_copy_blocks", "paged_kv_copy_blocks_workspace_size",
+    "paged_kv_append",
     "DEFAULT_PARTITION", "DEFAULT_PARTITION_GQA", "default_partition",
 ]
 
@@ -50,6 +51,8 @@ _SIGS = {
                                            _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                            ctypes.c_float, ctypes.c_int, _VP]),
     "paged_kv_copy_blocks_workspace_size": (_SZ, [_I64]),
+    "paged_kv_append": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32,
+                                        _I32, _I32, _I32, ctypes.c_int, _VP]),
     "paged_kv_copy_blocks": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64,
                                              _VP, _SZ, _VP]),
 }
@@ -203,6 +206,46 @@ def paged_attn_prefill(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Te
                                 _stream(stream))
     _check(st, "paged_attn_prefill")
     return out
+
+
+def paged_kv_append(k_cache: torch.Tensor, v_cache: Optional[torch.Tensor], key: torch.Tensor,
+                    value: Optional[torch.Tensor], block_tables: torch.Tensor,
+                    context_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                    stream=None) -> None:
+    """Write new tokens' K (and V) rows [T, Hkv, D] into the paged pools.
+
+    Sequence b's new tokens are rows query_start_loc[b]..query_start_loc[b+1]-1;
+    context_lens counts the tokens cached after the append, so new token i is
+    logical token context_lens[b] - q_b + i, stored in block
+    block_tables[b][pos // block_size] at row pos % block_size.
+    """
+    lib = load_library()
+    _need(key, "key", dims=3)
+    dt = key.dtype
+    if dt not in _DTYPE:
+        raise ValueError(f"unsupported dtype {dt}")
+    _need(k_cache, "k_cache", dt, 4)
+    if (v_cache is None) != (value is None):
+        raise ValueError("v_cache and value must both be given or both be None")
+    if v_cache is not None:
+        _need(v_cache, "v_cache", dt, 4)
+        _need(value, "value", dt, 3)
+        if v_cache.shape != k_cache.shape or value.shape != key.shape:
+            raise ValueError("K and V shapes differ")
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    _need(query_start_loc, "query_start_loc", torch.int32, 1)
+    T, Hkv, D = key.shape
+    nblk, Hkv_c, bs, D_c = k_cache.shape
+    B = context_lens.shape[0]
+    if (Hkv_c != Hkv or D_c != D or block_tables.shape[0] != B
+            or query_start_loc.shape[0] != B + 1):
+        raise ValueError("inconsistent shapes")
+    st = lib.paged_kv_append(_ptr(k_cache), _ptr(v_cache), _ptr(key), _ptr(value),
+                             _ptr(block_tables), _ptr(context_lens), _ptr(query_start_loc),
+                             B, T, Hkv, D, bs, nblk, block_tables.shape[1], _DTYPE[dt],
+                             _stream(stream))
+    _check(st, "paged_kv_append")
 
 
 def paged_kv_copy_blocks_workspace_size(num_dst_blocks: int) -> int:

@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedattn.so")
-SOURCES = ["abi.hip", "copy_blocks.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["abi.hip", "append.hip", "copy_blocks.hip", "decode.hip", "prefill.hip"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

@@ -213,6 +213,48 @@ pa_status_t paged_attn_prefill(void *out, const void *query, const void *k_cache
   return launch_status(pa::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
+pa_status_t paged_kv_append(void *k_cache, void *v_cache, const void *key, const void *value,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            const int32_t *query_start_loc, int32_t num_seqs,
+                            int32_t total_tokens, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                            pa_dtype_t dtype, void *stream) {
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
+  const int32_t elem = dtype == PA_DTYPE_F32 ? 4 : 2;
+  if (num_seqs < 0 || total_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return PA_ERR_SHAPE;
+  if ((head_dim * elem) % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (!pow2_in(block_size, 8, 256)) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)num_seqs * max_blocks_per_seq > INT32_MAX ||
+      (int64_t)max_blocks_per_seq * block_size > INT32_MAX ||
+      (int64_t)num_kv_heads * head_dim * elem > INT32_MAX / 2)
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0 || total_tokens == 0) return PA_OK;
+  if (!k_cache || !key || !block_tables || !context_lens || !query_start_loc) return PA_ERR_NULL;
+  if ((v_cache == nullptr) != (value == nullptr)) return PA_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(key) || (v_cache && (!aligned16(v_cache) || !aligned16(value))))
+    return PA_ERR_UNSUPPORTED;
+  if (!device_ok()) return PA_ERR_DEVICE;
+  pa::AppendLaunch a;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.key = key;
+  a.value = value;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = query_start_loc;
+  a.num_seqs = num_seqs;
+  a.total_tokens = total_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.elem_bytes = elem;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  return launch_status(pa::launch_append(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t paged_kv_copy_blocks_workspace_size(int64_t num_dst_blocks) {
   if (num_dst_blocks < 0) return 0;
   return (size_t)std::max<int64_t>(num_dst_blocks, 1) * sizeof(int32_t);

@@ -62,6 +62,16 @@ struct CopyLaunch {
 
 hipError_t launch_copy_blocks(const CopyLaunch &a, hipStream_t stream);
 
+struct AppendLaunch {
+  void *k_cache, *v_cache;       // v_cache NULL: K only
+  const void *key, *value;
+  const int32_t *block_tables, *context_lens, *query_start_loc;
+  int32_t num_seqs, total_tokens, num_kv_heads, head_dim, elem_bytes;
+  int32_t block_size, num_blocks, max_blocks_per_seq;
+};
+
+hipError_t launch_append(const AppendLaunch &a, hipStream_t stream);
+
 // Compute units of the current device (cached per device).
 int device_cu_count();
 

@@ -37,9 +37,10 @@ def declared_functions():
     return re.findall(r"^\s*(?:const\s+char\s*\*|size_t|pa_status_t)\s*(\w+)\s*\(", text, flags=re.M)
 
 
-def test_header_declares_the_three_operations():
+def test_header_declares_the_operations():
     names = declared_functions()
-    for n in ("paged_attn_decode", "paged_attn_prefill", "paged_kv_copy_blocks"):
+    for n in ("paged_attn_decode", "paged_attn_prefill", "paged_kv_copy_blocks",
+              "paged_kv_append"):
         assert n in names
 
 
@@ -209,3 +210,41 @@ def test_profile_events_must_be_paired(lib):
     assert lib.pa_set_profile_events(P, None) == PA_ERR_NULL
     assert lib.pa_set_profile_events(None, P) == PA_ERR_NULL
     assert lib.pa_set_profile_events(None, None) == PA_OK
+
+
+def _append(lib, **kw):
+    a = dict(k=P, v=P2, key=P3, value=P3 + 0x1000, bt=P, cl=P, qsl=P2, B=2, T=10, Hkv=2, D=128,
+             bs=16, nblk=64, mbps=8, dtype=2, stream=None)
+    a.update(kw)
+    return lib.paged_kv_append(a["k"], a["v"], a["key"], a["value"], a["bt"], a["cl"], a["qsl"],
+                               a["B"], a["T"], a["Hkv"], a["D"], a["bs"], a["nblk"], a["mbps"],
+                               a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=5), PA_ERR_DTYPE),
+    (dict(Hkv=0), PA_ERR_SHAPE),
+    (dict(B=-1), PA_ERR_SHAPE),
+    (dict(T=-1), PA_ERR_SHAPE),
+    (dict(nblk=0), PA_ERR_SHAPE),
+    (dict(mbps=0), PA_ERR_SHAPE),
+    (dict(D=4), PA_ERR_UNSUPPORTED),                 # 8-byte rows: not a multiple of 16
+    (dict(bs=12), PA_ERR_UNSUPPORTED),
+    (dict(bs=512), PA_ERR_UNSUPPORTED),
+    (dict(k=None), PA_ERR_NULL),
+    (dict(key=None), PA_ERR_NULL),
+    (dict(qsl=None), PA_ERR_NULL),
+    (dict(v=None), PA_ERR_NULL),                     # V pool without V rows
+    (dict(key=P3 + 8), PA_ERR_UNSUPPORTED),
+    (dict(B=0), PA_OK),
+    (dict(T=0), PA_OK),
+])
+def test_append_validation(lib, kw, want):
+    assert _append(lib, **kw) == want
+
+
+def test_append_reports_missing_device(lib):
+    if gpu_available():
+        pytest.skip("a GPU is present: valid arguments would launch")
+    assert _append(lib) == PA_ERR_DEVICE
+    assert _append(lib, v=None, value=None) == PA_ERR_DEVICE     # K only is valid

@@ -27,8 +27,8 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-from .work import (copy_bytes, copy_count_unique, decode_kv_bytes, kv_cache_bytes,  # noqa: F401
-                   prefill_flops, prefill_pairs)
+from .work import (append_bytes, copy_bytes, copy_count_unique, decode_kv_bytes,  # noqa: F401
+                   kv_cache_bytes, prefill_flops, prefill_pairs)
 
 DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
@@ -162,6 +162,36 @@ def make_prefill(prefix_lens, query_lens, num_heads: int, num_kv_heads: int, hea
 
 
 @dataclass
+class AppendInputs:
+    kv: PagedKV                     # pools written in place; tables cover prefix + new
+    key: torch.Tensor               # [T, Hkv, D] rows of the new tokens
+    value: torch.Tensor             # [T, Hkv, D]
+    query_start_loc: torch.Tensor   # int32 [B+1]
+    dtype: str
+    name: str = ""
+
+
+def make_append(prefix_lens, new_lens, num_kv_heads: int, head_dim: int, block_size: int,
+                dtype: str, seed: int, device="cpu", rng=None, name: str = "",
+                **kv_kw) -> AppendInputs:
+    """A paged pool whose tables already hold blocks for prefix + new tokens
+    (context_lens counts both), and fresh N(0,1) K/V rows for the new tokens."""
+    pre = np.asarray(prefix_lens, dtype=np.int64)
+    ql = np.asarray(new_lens, dtype=np.int64)
+    kv = make_paged_kv(pre + ql, num_kv_heads, head_dim, block_size, dtype, seed, device,
+                       rng=rng, **kv_kw)
+    qsl = np.zeros(len(ql) + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum(ql)
+    shape = (int(qsl[-1]), num_kv_heads, head_dim)
+    key = torch.empty(shape, dtype=DTYPES[dtype], device=device)
+    value = torch.empty(shape, dtype=DTYPES[dtype], device=device)
+    gen = _generator(seed + 104729, device)
+    _randn_fill(key, gen)
+    _randn_fill(value, gen)
+    return AppendInputs(kv, key, value, torch.as_tensor(qsl, device=device), dtype, name)
+
+
+@dataclass
 class CopyInputs:
     src_k: torch.Tensor
     src_v: torch.Tensor
@@ -199,7 +229,8 @@ def make_copy(num_src: int, num_dst: int, block_shape, dtype: str, seed: int, de
 
 
 # ---------------------------------------------------------------------------
-# The five named workloads.  Seeds 2481..2485.
+# The named workloads.  Seeds 2481..2486 (the append workload reuses the
+# prefill draw, 2485).
 # ---------------------------------------------------------------------------
 
 def tiny_decode_f32(device="cpu", **kw) -> DecodeInputs:
@@ -255,6 +286,18 @@ def prefill_bf16(device="cpu", num_seqs: int = 8, query_len: int = 2048, **kw) -
                         name="prefill_bf16", **kw)
 
 
+def append_bf16(device="cpu", num_seqs: int = 8, new_len: int = 2048, **kw) -> AppendInputs:
+    """KV append of the prefill workload's new tokens: 8 sequences each
+    appending 2048 tokens after cached prefixes uniform in [0, 8192] (the same
+    draw and pool as prefill_bf16), 8 kv heads, head_dim 128, block_size 16,
+    pool + 10% permuted, bf16; new rows N(0,1)."""
+    rng = np.random.default_rng(2485)
+    pre = rng.integers(0, 8192, size=num_seqs, endpoint=True)
+    ql = np.full(num_seqs, new_len, dtype=np.int64)
+    return make_append(pre, ql, 8, 128, 16, "bf16", 2485, device, rng=rng,
+                       name="append_bf16", **kw)
+
+
 def copy_bf16(device="cpu", **kw) -> CopyInputs:
     """Block copy of K and V pools: source pool 8192 blocks, destination pool
     4096 blocks of [8 heads, 16 slots, 128] bf16, mapping of length 4096 = a
@@ -269,4 +312,5 @@ WORKLOADS = {
     "long_decode_f16": long_decode_f16,
     "prefill_bf16": prefill_bf16,
     "copy_bf16": copy_bf16,
+    "append_bf16": append_bf16,
 }

@@ -58,3 +58,14 @@ def copy_count_unique(src_to_dst, num_src: int, num_dst: int) -> int:
     if np.unique(m[ok]).size != int(ok.sum()):
         raise ValueError("mapping names a destination more than once")
     return int((ok & (i < num_src)).sum())
+
+
+def append_bytes(num_tokens: int, num_seqs: int, num_kv_heads: int, head_dim: int,
+                 block_size: int, elem_bytes: int, pools: int = 2) -> int:
+    """Each new token's rows are read once and written once, in each pool (K
+    and V), plus the per-sequence metadata (query_start_loc, context_lens)
+    and one block-table entry per block-sized run of new tokens."""
+    rows = 2 * pools * num_tokens * num_kv_heads * head_dim * elem_bytes
+    meta = 4 * (num_seqs + 1) + 4 * num_seqs + 4 * ((num_tokens + block_size - 1) // block_size)
+    return rows + meta
+
