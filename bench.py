@@ -6,8 +6,9 @@ the LLaMA-7B-shaped decode workload: 64 sequences, 32 heads, head_dim 128,
 block_size 16, contexts uniform in [512, 4096], fp16, inputs resident in HBM.
 The headline value is its algorithmic KV bandwidth (GB/s).  The same run also
 measures the GQA bf16 and long-context split-KV decode workloads, the causal
-paged prefill (TFLOP/s), the block copy and the KV append (GB/s), and times the fp64 CPU
-oracle on a bounded sample of the headline workload.
+paged prefill (TFLOP/s), the block copy, the KV append and the host<->device
+swap (GB/s), and times the fp64 CPU oracle on a bounded sample of the
+headline workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
 
@@ -202,6 +203,41 @@ def bench_append(pa, torch, wl, case, steps, warmup):
     }
 
 
+def bench_swap(pa, torch, wl, case, steps, warmup):
+    """Swap out (device -> pinned host pools) and swap in (host -> device)
+    through paged_kv_copy_blocks; bytes are those crossing the host link (each
+    moved block of K and V once).  The link ceiling is a plain pinned copy of
+    the same size in each direction (the copy engines)."""
+    block_bytes = case.dev_k[0].numel() * case.dev_k.element_size()
+    ws = torch.empty(pa.paged_kv_copy_blocks_workspace_size(max(case.dev_k.shape[0],
+                                                                case.host_k.shape[0])),
+                     dtype=torch.uint8, device=case.dev_k.device)
+    res = {"workload": case.name, "block_bytes": block_bytes}
+    for direction in ("out", "in"):
+        if direction == "out":
+            args = (case.dev_k, case.dev_v, case.host_k, case.host_v, case.out_map)
+            n = wl.copy_count_unique(case.out_map.cpu().numpy(), case.dev_k.shape[0], case.host_k.shape[0])
+        else:
+            args = (case.host_k, case.host_v, case.dev_k, case.dev_v, case.in_map)
+            n = wl.copy_count_unique(case.in_map.cpu().numpy(), case.host_k.shape[0], case.dev_k.shape[0])
+        timer = KernelTimer(pa, torch, steps)
+        timed_steps(torch, lambda: pa.paged_kv_copy_blocks(*args, workspace=ws), steps, warmup, timer)
+        kms = timer.mean_ms()
+        nbytes = 2 * n * block_bytes
+        res[f"{direction}_kernel_ms"] = kms
+        res[f"{direction}_bytes"] = nbytes
+        res[f"{direction}_GBps"] = nbytes / (kms * 1e-3) / 1e9
+    # link ceiling: contiguous pinned <-> device copies of the swapped size
+    nb = res["out_bytes"]
+    host = torch.empty(nb, dtype=torch.uint8, pin_memory=True)
+    dev = torch.empty(nb, dtype=torch.uint8, device=case.dev_k.device)
+    for direction, fn in (("d2h", lambda: host.copy_(dev, non_blocking=True)),
+                          ("h2d", lambda: dev.copy_(host, non_blocking=True))):
+        ms = timed_steps(torch, fn, steps, warmup)
+        res[f"link_{direction}_GBps"] = nb / (ms * 1e-3) / 1e9
+    return res
+
+
 def bench_stream_copy(torch, steps, warmup, nbytes: int = 2 << 30):
     """A plain device-to-device copy of known size: the practical HBM ceiling
     for a read+write stream, and the reference that scales the FETCH_SIZE /
@@ -302,7 +338,8 @@ def main() -> int:
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--only", default=None, choices=["llama7b_decode_f16", "gqa_decode_bf16",
                                                        "long_decode_f16", "prefill_bf16",
-                                                       "copy_bf16", "append_bf16", "stream_copy"],
+                                                       "copy_bf16", "append_bf16", "swap_bf16",
+                                                       "stream_copy"],
                     help="run one workload, print its result object and exit (profiling)")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
@@ -339,6 +376,8 @@ def main() -> int:
             r = bench_copy(pa, torch, wl, case, args.steps, args.warmup)
         elif args.only.startswith("append"):
             r = bench_append(pa, torch, wl, case, args.steps, args.warmup)
+        elif args.only.startswith("swap"):
+            r = bench_swap(pa, torch, wl, case, max(5, args.steps // 10), max(5, args.warmup // 30))
         else:
             r = bench_decode(pa, torch, wl, case, args.steps, args.warmup)
         print(json.dumps(r), flush=True)
@@ -380,6 +419,14 @@ def main() -> int:
         log(f"  append: {r['kernel_ms']:.4f} ms, {r['kernel_GBps']:.0f} GB/s")
         extra["append_bf16"] = r
         del ac
+        torch.cuda.empty_cache()
+        log("generating swap_bf16 ...")
+        sc = wl.swap_bf16(device=dev)
+        r = bench_swap(pa, torch, wl, sc, max(5, args.steps // 10), max(5, args.warmup // 30))
+        log(f"  swap: out {r['out_GBps']:.1f} GB/s, in {r['in_GBps']:.1f} GB/s "
+            f"(plain pinned copies: d2h {r['link_d2h_GBps']:.1f}, h2d {r['link_h2d_GBps']:.1f})")
+        extra["swap_bf16"] = r
+        del sc
         torch.cuda.empty_cache()
 
     cpu = None

@@ -185,6 +185,16 @@ pa_status_t paged_attn_prefill(void *out, const void *query, const void *k_cache
  * ------------------------------------------------------------------------ */
 size_t paged_kv_copy_blocks_workspace_size(int64_t num_dst_blocks);
 
+/* Device-accessible address of pinned host memory allocated with
+ * hipHostMalloc (torch's pin_memory=True): with it, either pool pair of
+ * paged_kv_copy_blocks may live in host memory, which turns the block copy
+ * into the host<->device swap of [P-wall] §四.1 (swap out: device -> host
+ * pool; swap in: host -> device pool), the kernel reading or writing host
+ * memory over the host link.  Returns PA_ERR_NULL for NULL arguments and
+ * PA_ERR_UNSUPPORTED when host_ptr is not such memory (*device_ptr is then
+ * NULL). */
+pa_status_t pa_host_device_pointer(void *host_ptr, void **device_ptr);
+
 pa_status_t paged_kv_copy_blocks(const void *src_k, const void *src_v, void *dst_k,
                                  void *dst_v, const int64_t *src_to_dst, int64_t num_mappings,
                                  int64_t num_src_blocks, int64_t num_dst_blocks,

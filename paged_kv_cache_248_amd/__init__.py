@@ -51,6 +51,7 @@ _SIGS = {
                                            _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                            ctypes.c_float, ctypes.c_int, _VP]),
     "paged_kv_copy_blocks_workspace_size": (_SZ, [_I64]),
+    "pa_host_device_pointer": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_void_p)]),
     "paged_kv_append": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32,
                                         _I32, _I32, _I32, ctypes.c_int, _VP]),
     "paged_kv_copy_blocks": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64,
@@ -252,20 +253,43 @@ def paged_kv_copy_blocks_workspace_size(num_dst_blocks: int) -> int:
     return int(load_library().paged_kv_copy_blocks_workspace_size(num_dst_blocks))
 
 
+def _pool_ptr(t: Optional[torch.Tensor], name: str):
+    """Device-accessible address of a block pool: a device tensor, or a pinned
+    host tensor (the host side of a swap)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.is_cuda:
+        return _ptr(t)
+    if not t.is_pinned():
+        raise ValueError(f"{name} must be a device tensor or pinned host memory")
+    if t.numel() == 0:
+        return None
+    dev = ctypes.c_void_p()
+    st = load_library().pa_host_device_pointer(ctypes.c_void_p(t.data_ptr()), ctypes.byref(dev))
+    _check(st, "pa_host_device_pointer")
+    return dev
+
+
 def paged_kv_copy_blocks(src_k: torch.Tensor, src_v: Optional[torch.Tensor], dst_k: torch.Tensor,
                          dst_v: Optional[torch.Tensor], src_to_dst: torch.Tensor,
                          workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """dst[j] <- src[i] for src_to_dst[i] = j (lowest i per j, valid i only),
-    applied to the K pool pair and, if given, the V pool pair."""
+    applied to the K pool pair and, if given, the V pool pair.  Either pool
+    pair may be pinned host memory (swap out / swap in); src_to_dst and the
+    workspace are device tensors."""
     lib = load_library()
-    _need(src_k, "src_k")
-    _need(dst_k, "dst_k")
+    _pool_ptr(src_k, "src_k")
+    _pool_ptr(dst_k, "dst_k")
     _need(src_to_dst, "src_to_dst", torch.int64, 1)
     if (src_v is None) != (dst_v is None):
         raise ValueError("src_v and dst_v must both be given or both be None")
     if src_v is not None:
-        _need(src_v, "src_v")
-        _need(dst_v, "dst_v")
+        _pool_ptr(src_v, "src_v")
+        _pool_ptr(dst_v, "dst_v")
         if src_v.shape != src_k.shape or dst_v.shape != dst_k.shape:
             raise ValueError("K and V pools must have matching shapes")
     if src_k.shape[1:] != dst_k.shape[1:] or src_k.dtype != dst_k.dtype:
@@ -274,10 +298,11 @@ def paged_kv_copy_blocks(src_k: torch.Tensor, src_v: Optional[torch.Tensor], dst
     block_bytes = src_k[0].numel() * src_k.element_size() if num_src else dst_k[0].numel() * dst_k.element_size()
     need = paged_kv_copy_blocks_workspace_size(num_dst)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dst_k.device)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=src_to_dst.device)
     else:
         _need(workspace, "workspace", torch.uint8, 1)
-    st = lib.paged_kv_copy_blocks(_ptr(src_k), _ptr(src_v), _ptr(dst_k), _ptr(dst_v),
+    st = lib.paged_kv_copy_blocks(_pool_ptr(src_k, "src_k"), _pool_ptr(src_v, "src_v"),
+                                  _pool_ptr(dst_k, "dst_k"), _pool_ptr(dst_v, "dst_v"),
                                   _ptr(src_to_dst), src_to_dst.numel(), num_src, num_dst,
                                   block_bytes, _ptr(workspace), workspace.numel(),
                                   _stream(stream))

@@ -255,6 +255,18 @@ pa_status_t paged_kv_append(void *k_cache, void *v_cache, const void *key, const
   return launch_status(pa::launch_append(a, static_cast<hipStream_t>(stream)));
 }
 
+pa_status_t pa_host_device_pointer(void *host_ptr, void **device_ptr) {
+  if (!host_ptr || !device_ptr) return PA_ERR_NULL;
+  *device_ptr = nullptr;
+  void *d = nullptr;
+  if (hipHostGetDevicePointer(&d, host_ptr, 0) != hipSuccess || !d) {
+    (void)hipGetLastError();    // leave no sticky error for the next call
+    return PA_ERR_UNSUPPORTED;
+  }
+  *device_ptr = d;
+  return PA_OK;
+}
+
 size_t paged_kv_copy_blocks_workspace_size(int64_t num_dst_blocks) {
   if (num_dst_blocks < 0) return 0;
   return (size_t)std::max<int64_t>(num_dst_blocks, 1) * sizeof(int32_t);

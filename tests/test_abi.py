@@ -248,3 +248,14 @@ def test_append_reports_missing_device(lib):
         pytest.skip("a GPU is present: valid arguments would launch")
     assert _append(lib) == PA_ERR_DEVICE
     assert _append(lib, v=None, value=None) == PA_ERR_DEVICE     # K only is valid
+
+
+def test_host_device_pointer_rejects_null_and_plain_memory(lib):
+    out = ctypes.c_void_p(123)
+    assert lib.pa_host_device_pointer(None, ctypes.byref(out)) == PA_ERR_NULL
+    assert lib.pa_host_device_pointer(ctypes.c_void_p(P), None) == PA_ERR_NULL
+    buf = ctypes.create_string_buffer(4096)                 # ordinary, unpinned host memory
+    assert lib.pa_host_device_pointer(ctypes.cast(buf, ctypes.c_void_p), ctypes.byref(out)) == \
+        PA_ERR_UNSUPPORTED
+    assert not out.value
+

@@ -298,6 +298,60 @@ def append_bf16(device="cpu", num_seqs: int = 8, new_len: int = 2048, **kw) -> A
                        name="append_bf16", **kw)
 
 
+@dataclass
+class SwapInputs:
+    dev_k: torch.Tensor             # device pools [num_dev, *block_shape]
+    dev_v: torch.Tensor
+    host_k: torch.Tensor            # pinned host pools [num_host, *block_shape]
+    host_v: torch.Tensor
+    out_map: torch.Tensor           # int64 [num_dev] on the device: dev block i -> host block
+    in_map: torch.Tensor            # int64 [num_host] on the device: host block i -> dev block
+    name: str = ""
+
+
+def make_swap(num_dev: int, num_host: int, block_shape, dtype: str, seed: int, device="cuda",
+              invalid_frac: float = 0.1, name: str = "") -> SwapInputs:
+    """Device pools N(0,1), pinned host pools N(0,1) drawn after them (a
+    distinct pattern, so a swap in is visible); each mapping is a seeded
+    permutation of the other pool's block ids with ``invalid_frac`` of its
+    entries set to -1 (swap out: device block i -> host block out_map[i];
+    swap in: host block i -> device block in_map[i])."""
+    rng = np.random.default_rng(seed)
+
+    def mapping(n_from, n_to):
+        m = rng.permutation(max(n_from, n_to))[:n_from].astype(np.int64)
+        m[m >= n_to] = -1
+        bad = rng.choice(n_from, size=int(round(invalid_frac * n_from)), replace=False)
+        m[bad] = -1
+        return m
+
+    out_map, in_map = mapping(num_dev, num_host), mapping(num_host, num_dev)
+    dt = DTYPES[dtype]
+    gen = _generator(seed, device)
+    dev_k = torch.empty((num_dev, *block_shape), dtype=dt, device=device)
+    dev_v = torch.empty((num_dev, *block_shape), dtype=dt, device=device)
+    _randn_fill(dev_k, gen)
+    _randn_fill(dev_v, gen)
+    host_k = torch.empty((num_host, *block_shape), dtype=dt, pin_memory=True)
+    host_v = torch.empty((num_host, *block_shape), dtype=dt, pin_memory=True)
+    tmp = torch.empty((num_host, *block_shape), dtype=dt, device=device)
+    _randn_fill(tmp, gen)
+    host_k.copy_(tmp)
+    _randn_fill(tmp, gen)
+    host_v.copy_(tmp)
+    del tmp
+    return SwapInputs(dev_k, dev_v, host_k, host_v, torch.as_tensor(out_map, device=device),
+                      torch.as_tensor(in_map, device=device), name)
+
+
+def swap_bf16(device="cuda", **kw) -> SwapInputs:
+    """Host<->device swap of K and V blocks: 2048 device blocks and 2048
+    pinned host blocks of [8, 16, 128] bf16 (32 KiB per block per pool), each
+    mapping a seeded permutation with 10% -1 (1843 blocks moved per
+    direction)."""
+    return make_swap(2048, 2048, (8, 16, 128), "bf16", 2487, device, name="swap_bf16", **kw)
+
+
 def copy_bf16(device="cpu", **kw) -> CopyInputs:
     """Block copy of K and V pools: source pool 8192 blocks, destination pool
     4096 blocks of [8 heads, 16 slots, 128] bf16, mapping of length 4096 = a
@@ -313,4 +367,5 @@ WORKLOADS = {
     "prefill_bf16": prefill_bf16,
     "copy_bf16": copy_bf16,
     "append_bf16": append_bf16,
+    "swap_bf16": swap_bf16,
 }
