@@ -52,7 +52,9 @@ typedef enum {
                                partition size, alignment                        */
   PA_ERR_WORKSPACE = -5,    /* workspace NULL or smaller than the query says    */
   PA_ERR_LAUNCH = -6,       /* HIP reported an error while enqueueing           */
-  PA_ERR_DEVICE = -7        /* no usable HIP device is current                  */
+  PA_ERR_DEVICE = -7,       /* no usable HIP device is current                  */
+  PA_ERR_NO_BLOCKS = -8,    /* block manager: no free physical block            */
+  PA_ERR_REQUEST = -9       /* block manager: unknown or duplicate request id   */
 } pa_status_t;
 
 typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } pa_dtype_t;
@@ -237,6 +239,65 @@ pa_status_t paged_kv_append(void *k_cache, void *v_cache, const void *key, const
                             int32_t total_tokens, int32_t num_kv_heads, int32_t head_dim,
                             int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                             pa_dtype_t dtype, void *stream);
+
+/* --------------------------------------------------------------------------
+ * Host block manager ([P-wall] §三, the allocator simulator; §四.2, prefix
+ * sharing and copy-on-write): the producer of the block tables the kernels
+ * read.  Host memory only; no HIP call.  Not thread-safe: one manager is used
+ * by one thread at a time.
+ *
+ * Physical blocks 0 .. num_blocks-1 start free.  An allocation takes the
+ * lowest free id and gives it a reference count of 1; a release lowers the
+ * count and frees the block at 0.  A request's table lists its blocks in
+ * logical order and always holds ceil(tokens / block_size) of them.
+ *
+ *   pa_bm_create      num_blocks >= 1, block_size >= 1; *out receives the
+ *                     manager (free with pa_bm_destroy)
+ *   pa_bm_register    a new request with prompt_len tokens: allocates
+ *                     ceil(prompt_len / block_size) blocks.  PA_ERR_NO_BLOCKS
+ *                     (nothing kept) if they are not all free;
+ *                     PA_ERR_REQUEST if the id is in use
+ *   pa_bm_append_token  one more token: when the request's blocks are full a
+ *                     block is added; when its last block is partly filled
+ *                     and shared (count > 1) it is copied first: a new block
+ *                     replaces it in the table, the old one is released, and
+ *                     *cow_src / *cow_dst receive (old, new) so the caller can
+ *                     copy the block's K and V (paged_kv_copy_blocks); else
+ *                     both receive -1.  PA_ERR_NO_BLOCKS leaves the request
+ *                     unchanged
+ *   pa_bm_fork        child_id shares every block of parent_id (each count
+ *                     + 1) and starts with its token count (prefix sharing)
+ *   pa_bm_finish      releases every block of the request and forgets it
+ *   pa_bm_free_count  number of free blocks (or -1 for NULL)
+ *   pa_bm_block_table  copies up to `capacity` block ids of the request into
+ *                     blocks[], its block count into *num_blocks and its token
+ *                     count into *num_tokens (either may be NULL);
+ *                     PA_ERR_SHAPE if capacity is smaller than the count
+ *   pa_bm_free_list   the free block ids in increasing order (same contract)
+ *   pa_bm_ref_count   reference count of one block
+ *   pa_bm_fill_batch  the kernels' block_tables [n, max_blocks_per_seq]
+ *                     (unused entries -1) and context_lens [n] for a batch of
+ *                     requests, host arrays; PA_ERR_SHAPE if a request holds
+ *                     more than max_blocks_per_seq blocks
+ * ------------------------------------------------------------------------ */
+typedef struct pa_block_manager pa_block_manager;
+
+pa_status_t pa_bm_create(int32_t num_blocks, int32_t block_size, pa_block_manager **out);
+void pa_bm_destroy(pa_block_manager *bm);
+pa_status_t pa_bm_register(pa_block_manager *bm, int64_t request_id, int64_t prompt_len);
+pa_status_t pa_bm_append_token(pa_block_manager *bm, int64_t request_id, int32_t *cow_src,
+                               int32_t *cow_dst);
+pa_status_t pa_bm_fork(pa_block_manager *bm, int64_t parent_id, int64_t child_id);
+pa_status_t pa_bm_finish(pa_block_manager *bm, int64_t request_id);
+int32_t pa_bm_free_count(const pa_block_manager *bm);
+pa_status_t pa_bm_block_table(const pa_block_manager *bm, int64_t request_id, int32_t *blocks,
+                              int32_t capacity, int32_t *num_blocks, int64_t *num_tokens);
+pa_status_t pa_bm_free_list(const pa_block_manager *bm, int32_t *blocks, int32_t capacity,
+                            int32_t *num_blocks);
+pa_status_t pa_bm_ref_count(const pa_block_manager *bm, int32_t block, int32_t *count);
+pa_status_t pa_bm_fill_batch(const pa_block_manager *bm, const int64_t *request_ids,
+                             int32_t num_requests, int32_t max_blocks_per_seq,
+                             int32_t *block_tables, int32_t *context_lens);
 
 /* --------------------------------------------------------------------------
  * Measurement hook.

@@ -20,7 +20,7 @@ __all__ = [
     "paged_attn_decode", "paged_attn_decode_workspace_size",
     "paged_attn_prefill",
     "paged_kv_copy_blocks", "paged_kv_copy_blocks_workspace_size",
-    "paged_kv_append",
+    "paged_kv_append", "BlockManager", "OutOfBlocksError",
     "DEFAULT_PARTITION", "DEFAULT_PARTITION_GQA", "default_partition",
 ]
 
@@ -52,6 +52,18 @@ _SIGS = {
                                            ctypes.c_float, ctypes.c_int, _VP]),
     "paged_kv_copy_blocks_workspace_size": (_SZ, [_I64]),
     "pa_host_device_pointer": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_void_p)]),
+    "pa_bm_create": (ctypes.c_int, [_I32, _I32, ctypes.POINTER(ctypes.c_void_p)]),
+    "pa_bm_destroy": (None, [_VP]),
+    "pa_bm_register": (ctypes.c_int, [_VP, _I64, _I64]),
+    "pa_bm_append_token": (ctypes.c_int, [_VP, _I64, ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
+    "pa_bm_fork": (ctypes.c_int, [_VP, _I64, _I64]),
+    "pa_bm_finish": (ctypes.c_int, [_VP, _I64]),
+    "pa_bm_free_count": (_I32, [_VP]),
+    "pa_bm_block_table": (ctypes.c_int, [_VP, _I64, _VP, _I32, ctypes.POINTER(_I32),
+                                         ctypes.POINTER(_I64)]),
+    "pa_bm_free_list": (ctypes.c_int, [_VP, _VP, _I32, ctypes.POINTER(_I32)]),
+    "pa_bm_ref_count": (ctypes.c_int, [_VP, _I32, ctypes.POINTER(_I32)]),
+    "pa_bm_fill_batch": (ctypes.c_int, [_VP, _VP, _I32, _I32, _VP, _VP]),
     "paged_kv_append": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32,
                                         _I32, _I32, _I32, ctypes.c_int, _VP]),
     "paged_kv_copy_blocks": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64,
@@ -307,3 +319,99 @@ def paged_kv_copy_blocks(src_k: torch.Tensor, src_v: Optional[torch.Tensor], dst
                                   block_bytes, _ptr(workspace), workspace.numel(),
                                   _stream(stream))
     _check(st, "paged_kv_copy_blocks")
+
+
+class OutOfBlocksError(PagedAttnError):
+    """The block manager has no free physical block for the request."""
+
+
+class BlockManager:
+    """Host block manager of the paged KV cache (native, in the library):
+    allocation with reference counts from a sorted free list, per-request
+    block tables, growth one token at a time, prefix sharing (fork) and
+    copy-on-write.  Produces the block_tables / context_lens the kernels read.
+    """
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self._lib = load_library()
+        h = ctypes.c_void_p()
+        _check(self._lib.pa_bm_create(int(num_blocks), int(block_size), ctypes.byref(h)),
+               "pa_bm_create")
+        self._h = h
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.pa_bm_destroy(h)
+            self._h = None
+
+    def _st(self, st: int, what: str) -> None:
+        if st == -8:
+            raise OutOfBlocksError(st, what)
+        _check(st, what)
+
+    def register(self, request_id: int, prompt_len: int) -> None:
+        self._st(self._lib.pa_bm_register(self._h, int(request_id), int(prompt_len)), "register")
+
+    def append_token(self, request_id: int):
+        """None, or the (old, new) block pair of a copy-on-write."""
+        a, b = _I32(), _I32()
+        self._st(self._lib.pa_bm_append_token(self._h, int(request_id), ctypes.byref(a),
+                                              ctypes.byref(b)), "append_token")
+        return None if a.value < 0 else (a.value, b.value)
+
+    def fork(self, parent_id: int, child_id: int) -> None:
+        self._st(self._lib.pa_bm_fork(self._h, int(parent_id), int(child_id)), "fork")
+
+    def finish(self, request_id: int) -> None:
+        self._st(self._lib.pa_bm_finish(self._h, int(request_id)), "finish")
+
+    def free_count(self) -> int:
+        return int(self._lib.pa_bm_free_count(self._h))
+
+    def table(self, request_id: int) -> list:
+        n, t = _I32(), _I64()
+        # sizing call: PA_ERR_SHAPE (-3) only says the empty buffer is too small
+        st = self._lib.pa_bm_block_table(self._h, int(request_id), None, 0, ctypes.byref(n),
+                                         ctypes.byref(t))
+        if st not in (0, -3):
+            self._st(st, "table")
+        buf = (_I32 * max(n.value, 1))()
+        self._st(self._lib.pa_bm_block_table(self._h, int(request_id), buf, n.value,
+                                              ctypes.byref(n), ctypes.byref(t)), "table")
+        return list(buf[:n.value])
+
+    def tokens(self, request_id: int) -> int:
+        n, t = _I32(), _I64()
+        st = self._lib.pa_bm_block_table(self._h, int(request_id), None, 0, ctypes.byref(n),
+                                         ctypes.byref(t))
+        if st not in (0, -3):
+            self._st(st, "tokens")
+        return int(t.value)
+
+    def free_list(self) -> list:
+        buf = (_I32 * self.num_blocks)()
+        n = _I32()
+        self._st(self._lib.pa_bm_free_list(self._h, buf, self.num_blocks, ctypes.byref(n)),
+                 "free_list")
+        return list(buf[:n.value])
+
+    def ref_count(self, block: int) -> int:
+        c = _I32()
+        self._st(self._lib.pa_bm_ref_count(self._h, int(block), ctypes.byref(c)), "ref_count")
+        return int(c.value)
+
+    def batch_tables(self, request_ids, max_blocks_per_seq: int):
+        """(block_tables int32 [n, max_blocks_per_seq] with -1 padding,
+        context_lens int32 [n]) for the kernels, as CPU tensors."""
+        ids = torch.as_tensor(list(request_ids), dtype=torch.int64)
+        n = ids.numel()
+        tables = torch.empty((n, int(max_blocks_per_seq)), dtype=torch.int32)
+        lens = torch.empty(n, dtype=torch.int32)
+        self._st(self._lib.pa_bm_fill_batch(self._h, ctypes.c_void_p(ids.data_ptr()), n,
+                                            int(max_blocks_per_seq),
+                                            ctypes.c_void_p(tables.data_ptr()),
+                                            ctypes.c_void_p(lens.data_ptr())), "batch_tables")
+        return tables, lens
+

@@ -16,7 +16,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedattn.so")
-SOURCES = ["abi.hip", "append.hip", "copy_blocks.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["abi.hip", "append.hip", "block_manager.cpp", "copy_blocks.hip", "decode.hip",
+           "prefill.hip"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -29,7 +30,7 @@ CFLAGS = [
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, src.replace(".hip", ".o"))
+    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -38,7 +39,8 @@ def _compile(src: str) -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link the shared library; returns its path."""
+    """Compile every source (HIP kernels, host C++) and link the shared
+    library; returns its path."""
     os.makedirs(OBJ, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))

@@ -91,6 +91,8 @@ const char *pa_status_string(pa_status_t s) {
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: HIP reported an error while enqueueing";
     case PA_ERR_DEVICE: return "PA_ERR_DEVICE: no usable HIP device";
+    case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: no free physical block";
+    case PA_ERR_REQUEST: return "PA_ERR_REQUEST: unknown or duplicate request id";
   }
   return "PA_ERR_UNKNOWN";
 }

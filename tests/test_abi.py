@@ -16,6 +16,7 @@ HEADER = os.path.join(ROOT, "include", "paged_attn.h")
 
 PA_OK, PA_ERR_NULL, PA_ERR_DTYPE, PA_ERR_SHAPE = 0, -1, -2, -3
 PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_LAUNCH, PA_ERR_DEVICE = -4, -5, -6, -7
+PA_ERR_NO_BLOCKS, PA_ERR_REQUEST = -8, -9
 
 # Fake device addresses: only ever handed to calls that must fail on host
 # validation, before any HIP call could touch them.
@@ -54,8 +55,9 @@ def test_library_exports_every_declared_function(lib):
 
 def test_status_strings(lib):
     for s in (PA_OK, PA_ERR_NULL, PA_ERR_DTYPE, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED,
-              PA_ERR_WORKSPACE, PA_ERR_LAUNCH, PA_ERR_DEVICE):
+              PA_ERR_WORKSPACE, PA_ERR_LAUNCH, PA_ERR_DEVICE, PA_ERR_NO_BLOCKS, PA_ERR_REQUEST):
         assert lib.pa_status_string(s)
+        assert b"UNKNOWN" not in lib.pa_status_string(s)
     assert lib.pa_status_string(PA_OK) == b"PA_OK"
     assert b"UNKNOWN" in lib.pa_status_string(12345)
 

@@ -141,3 +141,41 @@ def test_append_rejects_bad_arguments():
     with pytest.raises(ValueError):
         pa.paged_kv_append(kv.k_cache, kv.v_cache, case.key[:, :1].contiguous(), case.value,
                            kv.block_tables, kv.context_lens, case.query_start_loc)
+
+
+def test_block_manager_tables_drive_append_and_decode():
+    """Prompts registered in the host block manager, a few generated tokens
+    appended one at a time (the manager adds blocks as they fill), the
+    manager's batch tables uploaded; every token's K/V written by the append
+    kernel; decode over the result equals the oracle on the same pool."""
+    from oracle import decode_ref
+    bs, Hkv, Hq, D, nblk = 16, 2, 8, 128, 64
+    bm = pa.BlockManager(nblk, bs)
+    prompts = {10: 37, 11: 1, 12: 64, 13: 5}
+    for rid, n in prompts.items():
+        bm.register(rid, n)
+    for _ in range(20):
+        for rid in (10, 13):
+            assert bm.append_token(rid) is None
+    rids = list(prompts)
+    tables, lens = bm.batch_tables(rids, 8)
+    assert lens.tolist() == [57, 1, 64, 25]
+    gen = torch.Generator(device=DEV).manual_seed(9)
+    kc = torch.full((nblk, Hkv, bs, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    vc = torch.full_like(kc, float("nan"))
+    T = int(lens.sum())
+    key = torch.randn((T, Hkv, D), generator=gen, device=DEV).to(torch.bfloat16)
+    value = torch.randn((T, Hkv, D), generator=gen, device=DEV).to(torch.bfloat16)
+    qsl = torch.zeros(len(rids) + 1, dtype=torch.int32)
+    qsl[1:] = torch.cumsum(lens, 0)
+    bt, cl, qs = tables.to(DEV), lens.to(DEV), qsl.to(DEV)
+    pa.paged_kv_append(kc, vc, key, value, bt, cl, qs)
+    q = torch.randn((len(rids), Hq, D), generator=gen, device=DEV).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    pa.paged_attn_decode(out, q, kc, vc, bt, cl, 1.0 / D ** 0.5, int(lens.max()))
+    torch.cuda.synchronize()
+    ref = decode_ref(q.float().cpu().numpy(), kc.float().cpu().numpy(), vc.float().cpu().numpy(),
+                     tables.numpy(), lens.numpy(), float(np.float32(1.0 / D ** 0.5)))
+    from tests._util import assert_close
+    assert_close(out.float().cpu().numpy(), ref, "bf16", "manager -> append -> decode")
+
