@@ -153,6 +153,46 @@ def bench_prefill(pa, torch, wl, case, steps, warmup):
     }
 
 
+def bench_prefill_unfused(pa, torch, wl, case, steps, warmup):
+    """The same prefill computed unfused (S and P through HBM, library
+    GEMMs); timed per call on the stream it runs on."""
+    kv = case.kv
+    out = torch.empty_like(case.query)
+    ctx = kv.context_lens.cpu()
+    qsl = case.query_start_loc.cpu()
+    ql = (qsl[1:] - qsl[:-1]).numpy()
+    T, Hq, D = case.query.shape
+    ws = torch.empty(pa.paged_attn_prefill_unfused_workspace_size(
+        int(ql.max()), int(ctx.max()), Hq, kv.k_cache.shape[1], D, case.query.dtype),
+        dtype=torch.uint8, device=case.query.device)
+
+    def step():
+        pa.paged_attn_prefill_unfused(out, case.query, kv.k_cache, kv.v_cache, kv.block_tables,
+                                      ctx, qsl, case.scale, workspace=ws)
+
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    c = ctx.numpy()
+    flops = wl.prefill_flops(c, ql, Hq, D)
+    e = wl.ELEM_BYTES[case.dtype]
+    # S (fp32) and P (dtype) of every head: written once and read once each
+    sp_bytes = int(sum(2 * Hq * int(q) * int(n) * (4 + e) for q, n in zip(ql, c)))
+    return {
+        "workload": case.name + " (unfused)", "ms_per_step": ms, "flops": flops,
+        "TFLOPs": flops / (ms * 1e-3) / 1e12, "tokens_per_s": T / (ms * 1e-3),
+        "s_p_hbm_bytes": sp_bytes, "steps": steps, "warmup": warmup,
+    }
+
+
 def bench_copy(pa, torch, wl, case, steps, warmup):
     n = wl.copy_count_unique(case.src_to_dst.cpu().numpy(), case.src_k.shape[0],
                              case.dst_k.shape[0])
@@ -339,7 +379,7 @@ def main() -> int:
     ap.add_argument("--only", default=None, choices=["llama7b_decode_f16", "gqa_decode_bf16",
                                                        "long_decode_f16", "prefill_bf16",
                                                        "copy_bf16", "append_bf16", "swap_bf16",
-                                                       "stream_copy"],
+                                                       "stream_copy", "prefill_unfused_bf16"],
                     help="run one workload, print its result object and exit (profiling)")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
@@ -366,6 +406,13 @@ def main() -> int:
 
     if args.only == "stream_copy":
         print(json.dumps(bench_stream_copy(torch, args.steps, args.warmup)), flush=True)
+        return 0
+    if args.only == "prefill_unfused_bf16":
+        log("generating prefill_bf16 ...")
+        case = wl.prefill_bf16(device=dev)
+        r = bench_prefill_unfused(pa, torch, wl, case, max(3, args.steps // 10),
+                                  max(2, args.warmup // 100))
+        print(json.dumps(r), flush=True)
         return 0
     if args.only:
         log(f"generating {args.only} ...")
@@ -405,7 +452,14 @@ def main() -> int:
         r = bench_prefill(pa, torch, wl, pc, args.steps, args.warmup)
         log(f"  prefill: {r['ms_per_step']:.3f} ms/step, {r['kernel_TFLOPs']:.0f} TFLOP/s")
         extra["prefill_bf16"] = r
+        u = bench_prefill_unfused(pa, torch, wl, pc, max(3, args.steps // 10),
+                                  max(2, args.warmup // 100))
+        u["fused_speedup"] = u["ms_per_step"] / r["ms_per_step"]
+        log(f"  unfused prefill: {u['ms_per_step']:.3f} ms/step, {u['TFLOPs']:.0f} TFLOP/s; "
+            f"fused is {u['fused_speedup']:.2f}x faster")
+        extra["prefill_unfused_bf16"] = u
         del pc
+        torch.cuda.empty_cache()
         log("generating copy_bf16 ...")
         cc = wl.copy_bf16(device=dev)
         r = bench_copy(pa, torch, wl, cc, args.steps, args.warmup)

@@ -8,6 +8,9 @@
  *                         the cached prefix and to each other;
  *   paged_kv_copy_blocks  copies whole cache blocks between two pools by a
  *                         src_to_dst mapping.
+ * Beside them: paged_kv_append (writes new tokens' K/V into their slots), a
+ * host block manager (pa_bm_*) that produces block tables, and
+ * paged_attn_prefill_unfused, the unfused baseline of prefill.
  *
  * Pages the operations follow (cited by title):
  *   [P-swap] "vLLM中FlashAttention与KVCache交换机制解析"
@@ -18,7 +21,10 @@
  * Conventions shared by every entry point
  *   - All array arguments are DEVICE pointers on the current HIP device,
  *     allocated and owned by the caller.  The library allocates and frees
- *     nothing and keeps no pointer after a call returns.
+ *     nothing and keeps no pointer after a call returns.  (Exceptions, stated
+ *     where they are declared: the block manager lives in host memory it
+ *     allocates, the unfused baseline takes host length arrays and creates a
+ *     matrix-library handle, and the copy accepts pinned host pools.)
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls only enqueue work: they return before the GPU finishes, never
  *     synchronise, and are safe to call from several host threads on
@@ -160,6 +166,55 @@ pa_status_t paged_attn_prefill(void *out, const void *query, const void *k_cache
                                int32_t block_size, int32_t num_blocks,
                                int32_t max_blocks_per_seq, float scale, pa_dtype_t dtype,
                                void *stream);
+
+/* --------------------------------------------------------------------------
+ * Unfused causal paged prefill (baseline).
+ *
+ * Computes exactly what paged_attn_prefill computes (same arguments, same
+ * causal alignment, same result within rounding) the way plain attention
+ * does it, which [P-wall] section 二.1 contrasts with FlashAttention: per
+ * sequence the full score matrix S = scale * Q K^T (fp32) is written to HBM,
+ * a row softmax with the causal mask reads it and writes P (input dtype),
+ * and O = P V reads P back; the [P-opt] FlashAttention table lists the
+ * stored P and the separate kernels as what fusion removes.  K and V are
+ * first gathered through the block table into contiguous scratch.  The two
+ * products are hipBLASLt GEMMs (fp32 accumulation).  It exists to measure
+ * the fused kernel against; it is not meant for serving.
+ *
+ *   out, query, k_cache, v_cache, block_tables  as for paged_attn_prefill
+ *                    (device)
+ *   context_lens_host    [num_seqs] int32, HOST memory: prefix + new keys
+ *   query_start_loc_host [num_seqs + 1] int32, HOST memory
+ *   workspace        device scratch of at least
+ *                    paged_attn_prefill_unfused_workspace_size(max q_b,
+ *                    max context_lens over sequences with q_b > 0, ...)
+ *                    bytes, 16-byte aligned; about
+ *                    Hq*q*n*(4 + e) + 2*Hkv*n*D*e + 2*q*Hq*D*e + 64 MiB
+ *                    (e = 2).  Calls sharing it must not overlap.
+ *
+ * The lengths live on the host because the library GEMMs take host-side
+ * shapes; their contents are validated (query_start_loc_host[0] = 0, last
+ * entry = total_query_tokens, 0 <= q_b <= context_lens_host[b] <=
+ * max_blocks_per_seq*block_size; else PA_ERR_SHAPE).  Supported: f16/bf16,
+ * head_dim 64 or 128, block_size a power of two in [8, 256], contexts of
+ * sequences with new tokens up to 32768 keys (else PA_ERR_UNSUPPORTED, as
+ * when the matrix library finds no kernel for a shape).  The first call on a
+ * device creates a hipBLASLt handle there, which lives until the process
+ * ends; a failure to create it is PA_ERR_DEVICE.  Work is enqueued on
+ * `stream` one sequence after another.
+ * ------------------------------------------------------------------------ */
+size_t paged_attn_prefill_unfused_workspace_size(int32_t max_query_len, int32_t max_context_len,
+                                                 int32_t num_heads, int32_t num_kv_heads,
+                                                 int32_t head_dim, pa_dtype_t dtype);
+pa_status_t paged_attn_prefill_unfused(void *out, const void *query, const void *k_cache,
+                                       const void *v_cache, const int32_t *block_tables,
+                                       const int32_t *context_lens_host,
+                                       const int32_t *query_start_loc_host, int32_t num_seqs,
+                                       int32_t total_query_tokens, int32_t num_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                       int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
+                                       pa_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                                       void *stream);
 
 /* --------------------------------------------------------------------------
  * Block copy by mapping.

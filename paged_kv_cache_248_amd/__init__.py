@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "PagedAttnError", "library_path", "load_library",
     "paged_attn_decode", "paged_attn_decode_workspace_size",
-    "paged_attn_prefill",
+    "paged_attn_prefill", "paged_attn_prefill_unfused", "paged_attn_prefill_unfused_workspace_size",
     "paged_kv_copy_blocks", "paged_kv_copy_blocks_workspace_size",
     "paged_kv_append", "BlockManager", "OutOfBlocksError",
     "DEFAULT_PARTITION", "DEFAULT_PARTITION_GQA", "default_partition",
@@ -50,6 +50,11 @@ _SIGS = {
     "paged_attn_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32,
                                            _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                            ctypes.c_float, ctypes.c_int, _VP]),
+    "paged_attn_prefill_unfused_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32,
+                                                        ctypes.c_int]),
+    "paged_attn_prefill_unfused": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32,
+                                                   _I32, _I32, _I32, _I32, _I32, _I32,
+                                                   ctypes.c_float, ctypes.c_int, _VP, _SZ, _VP]),
     "paged_kv_copy_blocks_workspace_size": (_SZ, [_I64]),
     "pa_host_device_pointer": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_void_p)]),
     "pa_bm_create": (ctypes.c_int, [_I32, _I32, ctypes.POINTER(ctypes.c_void_p)]),
@@ -218,6 +223,70 @@ def paged_attn_prefill(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Te
                                 nblk, block_tables.shape[1], float(scale), _DTYPE[dt],
                                 _stream(stream))
     _check(st, "paged_attn_prefill")
+    return out
+
+
+def paged_attn_prefill_unfused_workspace_size(max_query_len: int, max_context_len: int,
+                                              num_heads: int, num_kv_heads: int, head_dim: int,
+                                              dtype: torch.dtype) -> int:
+    return int(load_library().paged_attn_prefill_unfused_workspace_size(
+        int(max_query_len), int(max_context_len), int(num_heads), int(num_kv_heads),
+        int(head_dim), _DTYPE[dtype]))
+
+
+def _host_i32(t, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        t = torch.as_tensor(t)
+    if t.dtype != torch.int32 or t.dim() != 1:
+        raise ValueError(f"{name} must be a 1-D int32 tensor")
+    return t.cpu().contiguous()
+
+
+def paged_attn_prefill_unfused(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor,
+                               v_cache: torch.Tensor, block_tables: torch.Tensor,
+                               context_lens, query_start_loc, scale: float,
+                               workspace: Optional[torch.Tensor] = None,
+                               stream=None) -> torch.Tensor:
+    """Prefill computed the unfused way (S and P written to HBM): the
+    baseline of paged_attn_prefill, same arguments and result.
+
+    context_lens / query_start_loc are int32 vectors; the C call takes them in
+    host memory, so device tensors are copied to the host first (a sync).
+    workspace: uint8 device tensor of at least
+    paged_attn_prefill_unfused_workspace_size(...) bytes (allocated here if
+    None).
+    """
+    lib = load_library()
+    _need(query, "query", dims=3)
+    dt = query.dtype
+    if dt not in (torch.float16, torch.bfloat16):
+        raise ValueError(f"unsupported dtype {dt}")
+    _need(out, "out", dt, 3)
+    _need(k_cache, "k_cache", dt, 4)
+    _need(v_cache, "v_cache", dt, 4)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    cl = _host_i32(context_lens, "context_lens")
+    qsl = _host_i32(query_start_loc, "query_start_loc")
+    T, Hq, D = query.shape
+    nblk, Hkv, bs, Dk = k_cache.shape
+    B = cl.shape[0]
+    if (Dk != D or out.shape != query.shape or v_cache.shape != k_cache.shape
+            or block_tables.shape[0] != B or qsl.shape[0] != B + 1):
+        raise ValueError("inconsistent shapes")
+    ql = qsl[1:] - qsl[:-1]
+    live = ql > 0
+    max_q = int(ql.max()) if B else 0
+    max_ctx = int(cl[live].max()) if bool(live.any()) else 0
+    need = paged_attn_prefill_unfused_workspace_size(max_q, max_ctx, Hq, Hkv, D, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=query.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    st = lib.paged_attn_prefill_unfused(
+        _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        ctypes.c_void_p(cl.data_ptr()), ctypes.c_void_p(qsl.data_ptr()), B, T, Hq, Hkv, D, bs,
+        nblk, block_tables.shape[1], float(scale), _DTYPE[dt], _ptr(workspace),
+        workspace.numel(), _stream(stream))
+    _check(st, "paged_attn_prefill_unfused")
     return out
 
 

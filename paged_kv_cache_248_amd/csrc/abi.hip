@@ -215,6 +215,88 @@ pa_status_t paged_attn_prefill(void *out, const void *query, const void *k_cache
   return launch_status(pa::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t paged_attn_prefill_unfused_workspace_size(int32_t max_query_len, int32_t max_context_len,
+                                                 int32_t num_heads, int32_t num_kv_heads,
+                                                 int32_t head_dim, pa_dtype_t dtype) {
+  if ((dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) || max_query_len < 0 ||
+      max_context_len < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return 0;
+  return pa::unfused_workspace_layout(max_query_len, max_context_len, num_heads, num_kv_heads,
+                                      head_dim, 2)
+      .total;
+}
+
+pa_status_t paged_attn_prefill_unfused(void *out, const void *query, const void *k_cache,
+                                       const void *v_cache, const int32_t *block_tables,
+                                       const int32_t *context_lens_host,
+                                       const int32_t *query_start_loc_host, int32_t num_seqs,
+                                       int32_t total_query_tokens, int32_t num_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                       int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
+                                       pa_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                                       void *stream) {
+  if (dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || total_query_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+      num_heads % num_kv_heads != 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!pow2_in(block_size, 8, 256)) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)total_query_tokens * num_heads * head_dim > INT32_MAX ||
+      (int64_t)num_seqs * max_blocks_per_seq > INT32_MAX)
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0 || total_query_tokens == 0) return PA_OK;
+  if (!context_lens_host || !query_start_loc_host) return PA_ERR_NULL;
+  // The lengths are host arrays here (the library GEMMs take host-side
+  // shapes), so their contents are checked, not clamped.
+  if (query_start_loc_host[0] != 0 || query_start_loc_host[num_seqs] != total_query_tokens)
+    return PA_ERR_SHAPE;
+  int32_t max_q = 0, max_ctx = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int32_t q = query_start_loc_host[b + 1] - query_start_loc_host[b];
+    const int32_t n = context_lens_host[b];
+    if (q < 0 || n < q || (int64_t)n > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
+    if (q > 0 && n > pa::kUnfusedMaxContext) return PA_ERR_UNSUPPORTED;
+    max_q = std::max(max_q, q);
+    if (q > 0) max_ctx = std::max(max_ctx, n);
+  }
+  if (max_q == 0) return PA_OK;
+  if (!out || !query || !k_cache || !v_cache || !block_tables) return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+  if (!workspace || !aligned16(workspace) ||
+      workspace_bytes < paged_attn_prefill_unfused_workspace_size(max_q, max_ctx, num_heads,
+                                                                  num_kv_heads, head_dim, dtype))
+    return PA_ERR_WORKSPACE;
+  if (!device_ok()) return PA_ERR_DEVICE;
+  pa::UnfusedLaunch a;
+  a.out = out;
+  a.query = query;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens_host;
+  a.query_start_loc = query_start_loc_host;
+  a.num_seqs = num_seqs;
+  a.max_q = max_q;
+  a.max_ctx = max_ctx;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.scale = scale;
+  a.dtype = (pa::DType)dtype;
+  a.workspace = workspace;
+  switch (pa::launch_prefill_unfused(a, static_cast<hipStream_t>(stream))) {
+    case pa::PA_GEMM_OK: return PA_OK;
+    case pa::PA_GEMM_NO_HANDLE: return PA_ERR_DEVICE;
+    case pa::PA_GEMM_UNSUPPORTED: return PA_ERR_UNSUPPORTED;
+    default: return PA_ERR_LAUNCH;
+  }
+}
+
 pa_status_t paged_kv_append(void *k_cache, void *v_cache, const void *key, const void *value,
                             const int32_t *block_tables, const int32_t *context_lens,
                             const int32_t *query_start_loc, int32_t num_seqs,

@@ -72,6 +72,39 @@ struct AppendLaunch {
 
 hipError_t launch_append(const AppendLaunch &a, hipStream_t stream);
 
+// Unfused (S and P in HBM) causal prefill, the baseline of the fused kernel.
+struct UnfusedLaunch {
+  void *out;
+  const void *query;
+  const void *k_cache;
+  const void *v_cache;
+  const int32_t *block_tables;          // device
+  const int32_t *context_lens;          // host
+  const int32_t *query_start_loc;       // host
+  int32_t num_seqs, max_q, max_ctx;     // max_q / max_ctx over the sequences
+  int32_t num_heads, num_kv_heads, head_dim;
+  int32_t block_size, num_blocks, max_blocks_per_seq;
+  float scale;
+  DType dtype;
+  void *workspace;
+};
+
+// Scratch regions of one sequence (reused by the next): gathered K and V,
+// grouped Q and O, S (fp32) and P with rows padded to 8 elements, and the
+// matrix library's own workspace.
+struct UnfusedWorkspace {
+  size_t kg_off, vg_off, qg_off, og_off, s_off, p_off, blas_off, blas_bytes, total;
+};
+constexpr size_t kUnfusedBlasWorkspace = 64u << 20;
+// Longest context the unfused softmax keeps in registers (1024 x 32 keys).
+constexpr int32_t kUnfusedMaxContext = 32768;
+UnfusedWorkspace unfused_workspace_layout(int64_t max_q, int64_t max_ctx, int64_t num_heads,
+                                          int64_t num_kv_heads, int64_t head_dim,
+                                          int64_t elem_bytes);
+
+enum pa_gemm_status { PA_GEMM_OK = 0, PA_GEMM_NO_HANDLE, PA_GEMM_UNSUPPORTED, PA_GEMM_FAILED };
+pa_gemm_status launch_prefill_unfused(const UnfusedLaunch &a, hipStream_t stream);
+
 // Compute units of the current device (cached per device).
 int device_cu_count();
 

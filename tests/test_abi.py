@@ -261,3 +261,64 @@ def test_host_device_pointer_rejects_null_and_plain_memory(lib):
         PA_ERR_UNSUPPORTED
     assert not out.value
 
+
+
+def _i32(*vals):
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def _unfused(lib, **kw):
+    a = dict(out=P, query=P, k=P, v=P, bt=P, cl=_i32(30, 40), qsl=_i32(0, 4, 10), B=2, T=10, Hq=8,
+             Hkv=2, D=128, bs=16, nblk=64, mbps=8, scale=0.125, dtype=2, ws=P2, wsb=1 << 30,
+             stream=None)
+    a.update(kw)
+    return lib.paged_attn_prefill_unfused(
+        a["out"], a["query"], a["k"], a["v"], a["bt"],
+        ctypes.cast(a["cl"], ctypes.c_void_p) if a["cl"] is not None else None,
+        ctypes.cast(a["qsl"], ctypes.c_void_p) if a["qsl"] is not None else None,
+        a["B"], a["T"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["nblk"], a["mbps"], a["scale"],
+        a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=0), PA_ERR_DTYPE),
+    (dict(Hq=8, Hkv=3), PA_ERR_SHAPE),
+    (dict(D=96), PA_ERR_UNSUPPORTED),
+    (dict(bs=48), PA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), PA_ERR_UNSUPPORTED),
+    (dict(cl=None), PA_ERR_NULL),
+    (dict(qsl=None), PA_ERR_NULL),
+    (dict(qsl=_i32(1, 4, 10)), PA_ERR_SHAPE),          # does not start at 0
+    (dict(qsl=_i32(0, 4, 9)), PA_ERR_SHAPE),           # does not end at total_query_tokens
+    (dict(qsl=_i32(0, 6, 4), T=4), PA_ERR_SHAPE),      # decreasing
+    (dict(cl=_i32(3, 40)), PA_ERR_SHAPE),              # more new tokens than keys
+    (dict(cl=_i32(30, 129)), PA_ERR_SHAPE),            # more keys than the table maps
+    (dict(cl=_i32(30, 40000), mbps=4096), PA_ERR_UNSUPPORTED),   # beyond the softmax row limit
+    (dict(v=None), PA_ERR_NULL),
+    (dict(bt=None), PA_ERR_NULL),
+    (dict(k=P + 8), PA_ERR_UNSUPPORTED),
+    (dict(ws=None), PA_ERR_WORKSPACE),
+    (dict(wsb=1 << 20), PA_ERR_WORKSPACE),
+    (dict(T=0, qsl=_i32(0, 0, 0)), PA_OK),
+    (dict(B=0), PA_OK),
+])
+def test_unfused_validation(lib, kw, want):
+    assert _unfused(lib, **kw) == want
+
+
+def test_unfused_reports_missing_device(lib):
+    if gpu_available():
+        pytest.skip("a GPU is present: valid arguments would launch")
+    assert _unfused(lib) == PA_ERR_DEVICE
+
+
+def test_unfused_workspace_size(lib):
+    ws = lib.paged_attn_prefill_unfused_workspace_size
+    # S (fp32) and P (bf16) of 32 heads x 2048 rows x 8192 keys dominate
+    s_p = 32 * 2048 * 8192 * (4 + 2)
+    assert s_p < ws(2048, 8192, 32, 8, 128, 2) < s_p + (80 << 20) + 4 * 2048 * 32 * 128 * 2 + \
+        2 * 8 * 8192 * 128 * 2
+    # S/P rows are padded to 8 keys: 8190 and 8192 keys differ only in the gathered K/V
+    assert 0 < ws(2048, 8192, 32, 8, 128, 2) - ws(2048, 8190, 32, 8, 128, 2) <= 2 * 8 * 2 * 128 * 2
+    assert ws(16, 64, 8, 2, 64, 0) == 0            # fp32 is not provided
+    assert ws(-1, 64, 8, 2, 64, 2) == 0
