@@ -300,6 +300,28 @@ def bench_stream_copy(torch, steps, warmup, nbytes: int = 2 << 30):
             "ms": ms, "GBps": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
+def bench_stream_read(pa, torch, steps, warmup, nbytes: int = 4 << 30):
+    """A plain device read of known size (the library's read-stream probe):
+    the practical HBM ceiling for the read-dominated decode kernels."""
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    src.copy_(torch.arange(src.numel(), dtype=torch.int32, device="cuda:0"))
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    timer = KernelTimer(pa, torch, steps)
+    for _ in range(warmup):
+        pa.pa_stream_read(src, sink)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(steps):
+        timer.arm()
+        pa.pa_stream_read(src, sink)
+        timer.disarm()
+    torch.cuda.synchronize()
+    ts = [s.elapsed_time(e) for s, e in timer.pairs[:timer.i]]
+    ms = float(np.median(ts))
+    return {"workload": "stream_read", "bytes_read": nbytes, "ms": ms,
+            "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def cpu_baseline(torch, wl, case, budget_s: float, min_s: float = 10.0):
     """The fp64 oracle on the host cores, sequence by sequence, until the time
     budget is spent (whole passes are repeated until at least ``min_s``);
@@ -379,7 +401,7 @@ def main() -> int:
     ap.add_argument("--only", default=None, choices=["llama7b_decode_f16", "gqa_decode_bf16",
                                                        "long_decode_f16", "prefill_bf16",
                                                        "copy_bf16", "append_bf16", "swap_bf16",
-                                                       "stream_copy", "prefill_unfused_bf16"],
+                                                       "stream_copy", "stream_read", "prefill_unfused_bf16"],
                     help="run one workload, print its result object and exit (profiling)")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
@@ -406,6 +428,9 @@ def main() -> int:
 
     if args.only == "stream_copy":
         print(json.dumps(bench_stream_copy(torch, args.steps, args.warmup)), flush=True)
+        return 0
+    if args.only == "stream_read":
+        print(json.dumps(bench_stream_read(pa, torch, args.steps, args.warmup)), flush=True)
         return 0
     if args.only == "prefill_unfused_bf16":
         log("generating prefill_bf16 ...")
@@ -481,6 +506,10 @@ def main() -> int:
             f"(plain pinned copies: d2h {r['link_d2h_GBps']:.1f}, h2d {r['link_h2d_GBps']:.1f})")
         extra["swap_bf16"] = r
         del sc
+        torch.cuda.empty_cache()
+        r = bench_stream_read(pa, torch, min(args.steps, 50), min(args.warmup, 20))
+        log(f"  plain read stream: {r['GBps']:.0f} GB/s")
+        extra["stream_read"] = r
         torch.cuda.empty_cache()
 
     cpu = None

@@ -368,6 +368,21 @@ pa_status_t pa_bm_fill_batch(const pa_block_manager *bm, const int64_t *request_
  * ------------------------------------------------------------------------ */
 pa_status_t pa_set_profile_events(void *start, void *stop);
 
+/* --------------------------------------------------------------------------
+ * Read-stream probe (measurement only).
+ *
+ * Reads the `bytes` bytes at `src` (device, 16-byte aligned, bytes a
+ * multiple of 16, else PA_ERR_UNSUPPORTED) once with plain 16-byte loads
+ * spread over the whole GPU, and writes the XOR of all 32-bit words to
+ * sink[0] (device) only if it equals `magic`.  Its achieved GB/s is the
+ * practical HBM read ceiling that the read-dominated decode kernels are set
+ * beside (decode moves K/V once; the pages give their own HBM figure only
+ * for an older GPU, [P-wall] section 二, the HBM/SRAM diagram).  Recorded by
+ * pa_set_profile_events like a main kernel.
+ * ------------------------------------------------------------------------ */
+pa_status_t pa_stream_read(const void *src, int64_t bytes, uint32_t *sink, uint32_t magic,
+                           void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -322,3 +322,14 @@ def test_unfused_workspace_size(lib):
     assert 0 < ws(2048, 8192, 32, 8, 128, 2) - ws(2048, 8190, 32, 8, 128, 2) <= 2 * 8 * 2 * 128 * 2
     assert ws(16, 64, 8, 2, 64, 0) == 0            # fp32 is not provided
     assert ws(-1, 64, 8, 2, 64, 2) == 0
+
+
+def test_stream_read_validation(lib):
+    assert lib.pa_stream_read(P, -16, P2, 0, None) == PA_ERR_SHAPE
+    assert lib.pa_stream_read(P, 24, P2, 0, None) == PA_ERR_UNSUPPORTED     # not a multiple of 16
+    assert lib.pa_stream_read(P + 8, 32, P2, 0, None) == PA_ERR_UNSUPPORTED  # misaligned
+    assert lib.pa_stream_read(None, 32, P2, 0, None) == PA_ERR_NULL
+    assert lib.pa_stream_read(P, 32, None, 0, None) == PA_ERR_NULL
+    assert lib.pa_stream_read(P, 0, P2, 0, None) == PA_OK
+    if not gpu_available():
+        assert lib.pa_stream_read(P, 32, P2, 0, None) == PA_ERR_DEVICE
