@@ -305,7 +305,7 @@ def bench_stream_read(pa, torch, steps, warmup, nbytes: int = 4 << 30):
     the practical HBM ceiling for the read-dominated decode kernels."""
     src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda:0")
     src.copy_(torch.arange(src.numel(), dtype=torch.int32, device="cuda:0"))
-    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda:0")
     timer = KernelTimer(pa, torch, steps)
     for _ in range(warmup):
         pa.pa_stream_read(src, sink)

@@ -372,15 +372,17 @@ pa_status_t pa_set_profile_events(void *start, void *stop);
  * Read-stream probe (measurement only).
  *
  * Reads the `bytes` bytes at `src` (device, 16-byte aligned, bytes a
- * multiple of 16, else PA_ERR_UNSUPPORTED) once with plain 16-byte loads
- * spread over the whole GPU, and writes the XOR of all 32-bit words to
- * sink[0] (device) only if it equals `magic`.  Its achieved GB/s is the
- * practical HBM read ceiling that the read-dominated decode kernels are set
- * beside (decode moves K/V once; the pages give their own HBM figure only
- * for an older GPU, [P-wall] section 二, the HBM/SRAM diagram).  Recorded by
- * pa_set_profile_events like a main kernel.
+ * multiple of 16, else PA_ERR_UNSUPPORTED) once with non-temporal 16-byte
+ * loads spread over the whole GPU.  Work-group i writes the XOR of the 32-bit
+ * words it read to sink[i] (device, `sink_words` > 0 entries; at most that
+ * many work-groups run, and entries past the grid are left untouched), so
+ * the XOR of a zeroed sink after the call is the XOR of the whole buffer.
+ * Its achieved GB/s is the practical HBM read ceiling that the
+ * read-dominated decode kernels are set beside (decode moves K/V once; the
+ * pages give an HBM figure only for an older GPU, [P-wall] section 二, the
+ * HBM/SRAM diagram).  Recorded by pa_set_profile_events like a main kernel.
  * ------------------------------------------------------------------------ */
-pa_status_t pa_stream_read(const void *src, int64_t bytes, uint32_t *sink, uint32_t magic,
+pa_status_t pa_stream_read(const void *src, int64_t bytes, uint32_t *sink, int32_t sink_words,
                            void *stream);
 
 #ifdef __cplusplus

@@ -57,7 +57,7 @@ _SIGS = {
                                                    ctypes.c_float, ctypes.c_int, _VP, _SZ, _VP]),
     "paged_kv_copy_blocks_workspace_size": (_SZ, [_I64]),
     "pa_host_device_pointer": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_void_p)]),
-    "pa_stream_read": (ctypes.c_int, [_VP, _I64, _VP, ctypes.c_uint32, _VP]),
+    "pa_stream_read": (ctypes.c_int, [_VP, _I64, _VP, _I32, _VP]),
     "pa_bm_create": (ctypes.c_int, [_I32, _I32, ctypes.POINTER(ctypes.c_void_p)]),
     "pa_bm_destroy": (None, [_VP]),
     "pa_bm_register": (ctypes.c_int, [_VP, _I64, _I64]),
@@ -291,16 +291,15 @@ def paged_attn_prefill_unfused(out: torch.Tensor, query: torch.Tensor, k_cache: 
     return out
 
 
-def pa_stream_read(src: torch.Tensor, sink: torch.Tensor, magic: int = 0x9E3779B9,
-                   stream=None) -> None:
-    """Read every byte of `src` once on the GPU (measurement probe); `sink`
-    is an int32/uint32 device tensor written only if the XOR of all words
-    equals `magic`."""
+def pa_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Read every byte of `src` once on the GPU (measurement probe); work-group
+    i writes the XOR of the 32-bit words it read to sink[i] (int32 device
+    tensor; at most sink.numel() work-groups)."""
     lib = load_library()
     _need(src, "src")
-    _need(sink, "sink")
+    _need(sink, "sink", torch.int32, 1)
     _check(lib.pa_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
-                              int(magic) & 0xFFFFFFFF, _stream(stream)), "pa_stream_read")
+                              sink.numel(), _stream(stream)), "pa_stream_read")
 
 
 def paged_kv_append(k_cache: torch.Tensor, v_cache: Optional[torch.Tensor], key: torch.Tensor,

@@ -339,15 +339,16 @@ pa_status_t paged_kv_append(void *k_cache, void *v_cache, const void *key, const
   return launch_status(pa::launch_append(a, static_cast<hipStream_t>(stream)));
 }
 
-pa_status_t pa_stream_read(const void *src, int64_t bytes, uint32_t *sink, uint32_t magic,
+pa_status_t pa_stream_read(const void *src, int64_t bytes, uint32_t *sink, int32_t sink_words,
                            void *stream) {
-  if (bytes < 0) return PA_ERR_SHAPE;
+  if (bytes < 0 || sink_words <= 0) return PA_ERR_SHAPE;
   if (bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
   if (bytes == 0) return PA_OK;
   if (!src || !sink) return PA_ERR_NULL;
   if (!aligned16(src)) return PA_ERR_UNSUPPORTED;
   if (!device_ok()) return PA_ERR_DEVICE;
-  return launch_status(pa::launch_stream_read(src, bytes, sink, magic, static_cast<hipStream_t>(stream)));
+  return launch_status(
+      pa::launch_stream_read(src, bytes, sink, sink_words, static_cast<hipStream_t>(stream)));
 }
 
 pa_status_t pa_host_device_pointer(void *host_ptr, void **device_ptr) {

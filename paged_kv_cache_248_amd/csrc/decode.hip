@@ -268,8 +268,8 @@ __global__ __launch_bounds__(256, GT == 4 ? 4 : 2) void decode_kernel(DecodePara
         const int slot = min(ts + L * TPL + tok, end - 1) & (bs - 1);
         const size_t page_off = (size_t)ids[L] * block_stride;
         const uint32_t lane_off = (uint32_t)(slot * G::kRowBytes + chunk * 16);
-        kr[L] = ld16(kpage_base + page_off + lane_off);
-        vr[L] = ld16(vpage_base + page_off + lane_off);
+        kr[L] = ld16_nt(kpage_base + page_off + lane_off);
+        vr[L] = ld16_nt(vpage_base + page_off + lane_off);
       }
     };
     const float c = p.scale_log2e;
@@ -409,14 +409,15 @@ __global__ __launch_bounds__(256, GT == 4 ? 4 : 2) void decode_kernel(DecodePara
 // operand layout of the PV step, so the softmax output feeds it directly.
 // Each wavefront keeps three tiles in flight (K in registers, V in its own
 // LDS stages) and waits for each with an exact vmcnt count.
-// 16-byte global load at sbase + voff + OFF, issued as inline assembly: the
+// 16-byte non-temporal global load at sbase + voff + OFF (K is streamed
+// once), issued as inline assembly: the
 // compiler does not track it, so it inserts no wait of its own; the kernel
 // waits with an exact vmcnt and then ties the registers (tie_regs) before any
 // use.
 template <int OFF>
 __device__ __forceinline__ u32x4 gload16(const char *sbase, uint32_t voff) {
   u32x4 v;
-  asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3"
+  asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3 nt"
                : "=v"(v) : "v"(voff), "s"(sbase), "i"(OFF) : "memory");
   return v;
 }
@@ -557,7 +558,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
       for (int q = 0; q < VI; ++q) {
         const uint32_t voff = (uint32_t)((min(ts + v_row[q], end - 1) & (bs - 1)) * ROWB + v_chunk[q]);
-        dma16(vp + voff, my_v + buf * TILEB + q * 1024);
+        dma16_nt(vp + voff, my_v + buf * TILEB + q * 1024);
       }
     };
     // Tile loads still allowed in flight when tile t must have landed: the

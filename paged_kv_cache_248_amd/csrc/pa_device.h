@@ -58,6 +58,12 @@ __device__ __forceinline__ u32x4 ld16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+// Non-temporal 16-byte load (nt cache policy): for data streamed once, such
+// as K/V pages in decode.  On MI355X a read stream of such loads sustains
+// about 10% more HBM bandwidth than the same stream of plain loads.
+__device__ __forceinline__ u32x4 ld16_nt(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
 
 // ---- DPP lane exchange inside a row of 16 lanes ---------------------------
 // quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror.  Each step
@@ -155,6 +161,10 @@ __device__ __forceinline__ void wait_vm() {
 // (dst is the same for the whole wavefront).
 __device__ __forceinline__ void dma16(const void *src, char *dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+}
+// The same with the non-temporal cache policy (data streamed once).
+__device__ __forceinline__ void dma16_nt(const void *src, char *dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 2);
 }
 
 // MFMA operand reads from LDS, issued as inline assembly: the compiler does

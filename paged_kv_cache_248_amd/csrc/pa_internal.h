@@ -105,9 +105,9 @@ UnfusedWorkspace unfused_workspace_layout(int64_t max_q, int64_t max_ctx, int64_
 enum pa_gemm_status { PA_GEMM_OK = 0, PA_GEMM_NO_HANDLE, PA_GEMM_UNSUPPORTED, PA_GEMM_FAILED };
 pa_gemm_status launch_prefill_unfused(const UnfusedLaunch &a, hipStream_t stream);
 
-// Reads `bytes` (a multiple of 16) at src once; stores to sink only if the
-// XOR of all words equals magic.
-hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, uint32_t magic,
+// Reads `bytes` (a multiple of 16) at src once; work-group i writes the XOR
+// of the words it read to sink[i] (at most sink_words work-groups).
+hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, int32_t sink_words,
                               hipStream_t stream);
 
 // Compute units of the current device (cached per device).

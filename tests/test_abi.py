@@ -325,11 +325,12 @@ def test_unfused_workspace_size(lib):
 
 
 def test_stream_read_validation(lib):
-    assert lib.pa_stream_read(P, -16, P2, 0, None) == PA_ERR_SHAPE
-    assert lib.pa_stream_read(P, 24, P2, 0, None) == PA_ERR_UNSUPPORTED     # not a multiple of 16
-    assert lib.pa_stream_read(P + 8, 32, P2, 0, None) == PA_ERR_UNSUPPORTED  # misaligned
-    assert lib.pa_stream_read(None, 32, P2, 0, None) == PA_ERR_NULL
-    assert lib.pa_stream_read(P, 32, None, 0, None) == PA_ERR_NULL
-    assert lib.pa_stream_read(P, 0, P2, 0, None) == PA_OK
+    assert lib.pa_stream_read(P, -16, P2, 8, None) == PA_ERR_SHAPE
+    assert lib.pa_stream_read(P, 32, P2, 0, None) == PA_ERR_SHAPE            # no sink entries
+    assert lib.pa_stream_read(P, 24, P2, 8, None) == PA_ERR_UNSUPPORTED     # not a multiple of 16
+    assert lib.pa_stream_read(P + 8, 32, P2, 8, None) == PA_ERR_UNSUPPORTED  # misaligned
+    assert lib.pa_stream_read(None, 32, P2, 8, None) == PA_ERR_NULL
+    assert lib.pa_stream_read(P, 32, None, 8, None) == PA_ERR_NULL
+    assert lib.pa_stream_read(P, 0, P2, 8, None) == PA_OK
     if not gpu_available():
-        assert lib.pa_stream_read(P, 32, P2, 0, None) == PA_ERR_DEVICE
+        assert lib.pa_stream_read(P, 32, P2, 8, None) == PA_ERR_DEVICE
