@@ -193,6 +193,52 @@ def bench_prefill_unfused(pa, torch, wl, case, steps, warmup):
     }
 
 
+def bench_tiny_decode(pa, torch, wl, steps, warmup):
+    """The tiny fp32 decode (4 sequences, contexts up to 200 tokens): a
+    launch-bound call, reported in microseconds per call, issued eagerly and
+    as the replay of a captured HIP graph (its launches recorded once)."""
+    case = wl.tiny_decode_f32(device="cuda:0")
+    kv = case.kv
+    out = torch.empty_like(case.query)
+    B, Hq, D = case.query.shape
+    maxctx = kv.max_context_len
+    ws = torch.empty(max(1, pa.paged_attn_decode_workspace_size(B, Hq, kv.k_cache.shape[1], D,
+                                                                maxctx, 0)),
+                     dtype=torch.uint8, device="cuda:0")
+
+    def call():
+        pa.paged_attn_decode(out, case.query, kv.k_cache, kv.v_cache, kv.block_tables,
+                             kv.context_lens, case.scale, maxctx, workspace=ws)
+
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        call()
+    stop.record()
+    torch.cuda.synchronize()
+    eager_us = start.elapsed_time(stop) * 1e3 / steps
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    graph_us = start.elapsed_time(stop) * 1e3 / steps
+    ctx = kv.context_lens.cpu().numpy()
+    return {"workload": "tiny_decode_f32", "eager_us_per_call": eager_us,
+            "graph_us_per_call": graph_us, "num_seqs": B, "num_heads": Hq, "head_dim": D,
+            "context_lens": ctx.tolist(), "steps": steps, "warmup": warmup}
+
+
 def bench_copy(pa, torch, wl, case, steps, warmup):
     n = wl.copy_count_unique(case.src_to_dst.cpu().numpy(), case.src_k.shape[0],
                              case.dst_k.shape[0])
@@ -401,7 +447,8 @@ def main() -> int:
     ap.add_argument("--only", default=None, choices=["llama7b_decode_f16", "gqa_decode_bf16",
                                                        "long_decode_f16", "prefill_bf16",
                                                        "copy_bf16", "append_bf16", "swap_bf16",
-                                                       "stream_copy", "stream_read", "prefill_unfused_bf16"],
+                                                       "stream_copy", "stream_read", "prefill_unfused_bf16",
+                                                       "tiny_decode_f32"],
                     help="run one workload, print its result object and exit (profiling)")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
@@ -428,6 +475,9 @@ def main() -> int:
 
     if args.only == "stream_copy":
         print(json.dumps(bench_stream_copy(torch, args.steps, args.warmup)), flush=True)
+        return 0
+    if args.only == "tiny_decode_f32":
+        print(json.dumps(bench_tiny_decode(pa, torch, wl, args.steps, args.warmup)), flush=True)
         return 0
     if args.only == "stream_read":
         print(json.dumps(bench_stream_read(pa, torch, args.steps, args.warmup)), flush=True)
@@ -463,6 +513,10 @@ def main() -> int:
 
     extra = {}
     if not args.quick:
+        r = bench_tiny_decode(pa, torch, wl, args.steps, min(args.warmup, 50))
+        log(f"  tiny_decode_f32: {r['eager_us_per_call']:.1f} us/call eager, "
+            f"{r['graph_us_per_call']:.1f} us/call as a graph replay")
+        extra["tiny_decode_f32"] = r
         for name in ("gqa_decode_bf16", "long_decode_f16"):
             log(f"generating {name} ...")
             case = wl.WORKLOADS[name](device=dev)

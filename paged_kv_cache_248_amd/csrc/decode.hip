@@ -78,6 +78,9 @@ struct DecodeParams {
   int32_t num_heads, num_kv_heads, group, head_chunks;
   int32_t bs_log2, max_blocks_per_seq, num_blocks;
   int32_t partition, max_parts, ctx_cap;
+  // 1: every sequence fits one partition; work-group i takes item i (items
+  // numbered (sequence, kv head, head chunk)) and there is no work list.
+  int32_t direct;
   float scale_log2e;
 };
 
@@ -193,20 +196,27 @@ __global__ __launch_bounds__(256, GT == 4 ? 4 : 2) void decode_kernel(DecodePara
   const char *vbase = static_cast<const char *>(p.v_cache);
   const size_t head_stride = (size_t)bs * G::kRowBytes;          // one (block, head) page
   const size_t block_stride = head_stride * (size_t)Hkv;
-  const int total = as_const(p.work_count)[0] * Hkv * p.head_chunks;
+  const int total = p.direct ? (int)gridDim.x : as_const(p.work_count)[0] * Hkv * p.head_chunks;
 
-  for (;;) {
-    if (tid == 0) s_item = atomicAdd(p.next_item, 1);
-    __syncthreads();
-    const int item = s_item;
+  for (int round = 0;; ++round) {
+    int item;
+    if (p.direct) {
+      if (round > 0) break;
+      item = blockIdx.x;
+    } else {
+      if (tid == 0) s_item = atomicAdd(p.next_item, 1);
+      __syncthreads();
+      item = s_item;
+    }
     if (item >= total) break;
     const int hc = item % p.head_chunks;
     const int rest = item / p.head_chunks;
     const int g = rest % Hkv;
     const int wi = rest / Hkv;
-    const int b = as_const(p.work)[2 * wi];
-    const int part = as_const(p.work)[2 * wi + 1];
+    const int b = p.direct ? wi : as_const(p.work)[2 * wi];
+    const int part = p.direct ? 0 : as_const(p.work)[2 * wi + 1];
     const int ctx = min(max(as_const(p.context_lens)[b], 0), p.ctx_cap);
+    if (ctx == 0) break;            // direct items only (the work list holds no empty sequence)
     const int start = part * p.partition;
     const int end = min(start + p.partition, ctx);
     const int nparts = (ctx + p.partition - 1) / p.partition;
@@ -472,7 +482,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeParams p) {
   const int Hq = p.num_heads, Hkv = p.num_kv_heads;
   const size_t head_stride = (size_t)bs * ROWB;
   const size_t block_stride = head_stride * (size_t)Hkv;
-  const int total = as_const(p.work_count)[0] * Hkv * p.head_chunks;
+  const int total = p.direct ? (int)gridDim.x : as_const(p.work_count)[0] * Hkv * p.head_chunks;
 
   // V stages: row r of a tile holds its 16-byte chunk c at position
   // c ^ vsw(r), vsw(r) = 2 (r mod 8) for 256-byte rows and 2 ((r / 2) mod 4)
@@ -500,18 +510,25 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeParams p) {
     v_chunk[q] = ((lane % CPR) ^ vsw(v_row[q])) * 16;
   }
 
-  for (;;) {
-    if (tid == 0) s_item = atomicAdd(p.next_item, 1);
-    __syncthreads();
-    const int item = s_item;
+  for (int round = 0;; ++round) {
+    int item;
+    if (p.direct) {
+      if (round > 0) break;
+      item = blockIdx.x;
+    } else {
+      if (tid == 0) s_item = atomicAdd(p.next_item, 1);
+      __syncthreads();
+      item = s_item;
+    }
     if (item >= total) break;
     const int hc = item % p.head_chunks;
     const int rest = item / p.head_chunks;
     const int g = rest % Hkv;
     const int wi = rest / Hkv;
-    const int b = as_const(p.work)[2 * wi];
-    const int part = as_const(p.work)[2 * wi + 1];
+    const int b = p.direct ? wi : as_const(p.work)[2 * wi];
+    const int part = p.direct ? 0 : as_const(p.work)[2 * wi + 1];
     const int ctx = min(max(as_const(p.context_lens)[b], 0), p.ctx_cap);
+    if (ctx == 0) break;            // direct items only (the work list holds no empty sequence)
     const int start = part * p.partition;
     const int end = min(start + p.partition, ctx);
     const int nparts = (ctx + p.partition - 1) / p.partition;
@@ -847,10 +864,15 @@ hipError_t launch_typed(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStr
   p.max_parts = a.max_parts;
   p.ctx_cap = a.ctx_cap;
   p.scale_log2e = a.scale * kLog2e;
+  // A single partition per sequence needs neither the work list nor the
+  // dynamic counter: one work-group per item, launched directly.
+  p.direct = a.max_parts == 1;
 
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, a.context_lens,
-                     a.num_seqs, a.partition, a.ctx_cap, reinterpret_cast<int32_t *>(w + ws.work_off),
-                     reinterpret_cast<int32_t *>(w + ws.count_off), p.next_item);
+  if (!p.direct)
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, a.context_lens,
+                       a.num_seqs, a.partition, a.ctx_cap,
+                       reinterpret_cast<int32_t *>(w + ws.work_off),
+                       reinterpret_cast<int32_t *>(w + ws.count_off), p.next_item);
 
   // Resident work-groups per CU; items are fetched dynamically, so a grid
   // larger than what fits only queues (it cannot unbalance the work).
@@ -868,7 +890,8 @@ hipError_t launch_typed(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStr
   const long long upper =
       (long long)a.num_seqs * a.max_parts * a.num_kv_heads * p.head_chunks;
   const long long resident = (long long)device_cu_count() * occ;
-  const int grid = (int)std::max(1LL, std::min(upper, resident));
+  const int grid = p.direct ? (int)std::max(1LL, upper)
+                            : (int)std::max(1LL, std::min(upper, resident));
   profile_begin(stream);
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, stream, p);
   profile_end(stream);

@@ -218,3 +218,41 @@ def test_empty_batch_is_a_no_op():
     pa.paged_attn_decode(q, q, kc, kc, torch.zeros(0, 2, dtype=torch.int32, device=DEV),
                          torch.zeros(0, dtype=torch.int32, device=DEV), 0.125, 32)
     torch.cuda.synchronize()
+
+
+def test_tiny_decode_graph_replays_match_eager():
+    """Decode captured into a HIP graph (plan + attention launches, no memset
+    nodes): every replay, with new query values written into the captured
+    input between replays and eager work interleaved, equals the eager call
+    on the same inputs bit for bit."""
+    case = wl.tiny_decode_f32(device=DEV, poison=True)
+    kv = case.kv
+    B, Hq, D = case.query.shape
+    maxctx = kv.max_context_len            # host value, read before the capture
+    ws = torch.empty(max(1, pa.paged_attn_decode_workspace_size(B, Hq, kv.k_cache.shape[1], D,
+                                                                maxctx, 0)),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(case.query)
+
+    def call(o, w):
+        pa.paged_attn_decode(o, case.query, kv.k_cache, kv.v_cache, kv.block_tables,
+                             kv.context_lens, case.scale, maxctx, workspace=w)
+
+    call(out, ws)                          # first call outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out, ws)
+    gen = torch.Generator(device="cpu").manual_seed(9)
+    eager_out = torch.empty_like(out)
+    eager_ws = torch.empty_like(ws)
+    for r in range(4):
+        case.query.copy_(torch.randn(case.query.shape, generator=gen).to(DEV))
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        call(eager_out, eager_ws)          # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out), f"replay {r}"
+    ref = oracle_full(case)
+    assert_close(host(out), ref, "f32", "graph replay")
