@@ -510,9 +510,14 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
         if (kt == 0) load_tile(lt, ids, 0, IPW / 2);
         else load_tile(lt, ids, IPW / 2, IPW);
       };
+      // The wavefront in its matrix phase runs at raised issue priority, so
+      // that its operand reads and MFMAs win the SIMD's arbitration against
+      // the softmax wavefront beside it (measured +0.3%, same box A/B).
       if constexpr (GRP == 0) {
         ids_tie(ids);                                     // phase 2j
+        __builtin_amdgcn_s_setprio(1);
         matrix_phase(kb, vb, pv, between);
+        __builtin_amdgcn_s_setprio(0);
         phase_sync();
         ids = fetch_ids(lt + 1);                          // phase 2j+1
         if (qk) softmax(j);
@@ -523,7 +528,9 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
         if (pv) softmax(j - 1);
         phase_sync();
         ids_tie(ids);                                     // phase 2j+1
+        __builtin_amdgcn_s_setprio(1);
         matrix_phase(kb, vb, pv, between);
+        __builtin_amdgcn_s_setprio(0);
         wait_vm<kWaitSteady>();
         phase_sync();
       }
