@@ -256,3 +256,27 @@ def test_tiny_decode_graph_replays_match_eager():
         assert torch.equal(out, eager_out), f"replay {r}"
     ref = oracle_full(case)
     assert_close(host(out), ref, "f32", "graph replay")
+
+
+@pytest.mark.parametrize("dtype,long_ctx", [("f32", False), ("f16", True), ("bf16", True)])
+def test_empty_contexts_leave_their_rows_unwritten(dtype, long_ctx):
+    """context_lens of 0 or below: that sequence's output rows keep their
+    previous bytes, in the single-partition launch (all contexts short) and
+    in the split launch (one context spans several partitions); the other
+    rows match the oracle."""
+    ctx = np.array([40, 3, 700 if long_ctx else 90, 17])
+    Hq, Hkv = (8, 2) if dtype != "f32" else (4, 4)
+    case = wl.make_decode(ctx, Hq, Hkv, 128, 16, dtype, seed=31, device=DEV)
+    kv = case.kv
+    cl = kv.context_lens.clone()
+    cl[1] = 0
+    cl[3] = -5
+    out = torch.full_like(case.query, 7.0)
+    pa.paged_attn_decode(out, case.query, kv.k_cache, kv.v_cache, kv.block_tables, cl,
+                         case.scale, int(ctx.max()), partition_size=256 if long_ctx else 0)
+    torch.cuda.synchronize()
+    got = host(out)
+    assert (got[1] == 7.0).all() and (got[3] == 7.0).all()
+    ref = decode_ref(host(case.query), host(kv.k_cache), host(kv.v_cache), host(kv.block_tables),
+                     host(kv.context_lens), case.scale)
+    assert_close(got[[0, 2]], ref[[0, 2]], dtype, "rows with keys")
