@@ -415,6 +415,56 @@ def cpu_baseline(torch, wl, case, budget_s: float, min_s: float = 10.0):
     }
 
 
+def cpu_prefill_sample(torch, wl, case, budget_s: float = 5.0):
+    """The fp64 prefill oracle on the host cores over a bounded sample of the
+    prefill workload: every 32nd new-token row of its shortest sequence, all
+    heads, repeated until ``budget_s``; reported in GFLOP/s of the visible
+    (query, key) pairs, the formula the GPU figure uses."""
+    from oracle import prefill_ref
+    kv = case.kv
+    ctx = kv.context_lens.cpu().numpy()
+    qsl = case.query_start_loc.cpu().numpy()
+    b = int(np.argmin(ctx))
+    n = int(ctx[b])
+    q_b = int(qsl[b + 1] - qsl[b])
+    nb = (n + kv.block_size - 1) // kv.block_size
+    ids = kv.block_tables[b, :nb].long()
+    k = kv.k_cache.index_select(0, ids).float().cpu().numpy()
+    v = kv.v_cache.index_select(0, ids).float().cpu().numpy()
+    q = case.query[int(qsl[b]):int(qsl[b + 1])].float().cpu().numpy()
+    rows = np.arange(0, q_b, 32)
+    T, Hq, D = case.query.shape
+    pairs = int(sum(n - q_b + int(t) + 1 for t in rows))
+    flops_per_call = 4 * D * Hq * pairs
+    calls, spent = 0, 0.0
+    while spent < budget_s and calls < 20:
+        t0 = time.perf_counter()
+        prefill_ref(q, k, v, np.arange(nb, dtype=np.int32)[None], np.array([n]),
+                    np.array([0, q_b]), case.scale, rows=rows)
+        spent += time.perf_counter() - t0
+        calls += 1
+    return {"value": flops_per_call * calls / spent / 1e9, "unit": "GFLOP/s", "kind": "oracle",
+            "sample": f"{len(rows)} of the {q_b} new-token rows (every 32nd) of the shortest "
+                      f"sequence ({n} keys), all {Hq} heads, {calls} call(s), {spent:.1f} s of fp64 numpy"}
+
+
+def cpu_copy_sample(torch, wl, case):
+    """The block-copy oracle on the host cores over the whole copy workload
+    (K and V pools, one call each), in GB/s of the copy formula."""
+    from oracle import copy_blocks_ref
+    m = case.src_to_dst.cpu().numpy()
+    n = wl.copy_count_unique(m, case.src_k.shape[0], case.dst_k.shape[0])
+    block_bytes = case.src_k[0].numel() * case.src_k.element_size()
+    host = [t.cpu().view(torch.int16).numpy() for t in (case.src_k, case.dst_k, case.src_v, case.dst_v)]
+    t0 = time.perf_counter()
+    copy_blocks_ref(host[0], host[1], m)
+    copy_blocks_ref(host[2], host[3], m)
+    spent = time.perf_counter() - t0
+    return {"value": wl.copy_bytes(n, block_bytes) / spent / 1e9, "unit": "GB/s", "kind": "oracle",
+            "sample": f"the whole {case.name or 'copy'} workload ({n} blocks of K and of V), "
+                      f"{spent:.2f} s"}
+
+
 def hbm_traffic(kernel_files, launches_key: str):
     """Calibrated HBM bytes per launch from the committed PMC summary, or None
     when the kernel sources changed since the counters were taken."""
@@ -512,6 +562,7 @@ def main() -> int:
         f"(kernel {res['kernel_ms']:.3f} ms, {res['kernel_GBps']:.0f} GB/s)")
 
     extra = {}
+    cpu_other = {}
     if not args.quick:
         r = bench_tiny_decode(pa, torch, wl, args.steps, min(args.warmup, 50))
         log(f"  tiny_decode_f32: {r['eager_us_per_call']:.1f} us/call eager, "
@@ -537,6 +588,10 @@ def main() -> int:
         log(f"  unfused prefill: {u['ms_per_step']:.3f} ms/step, {u['TFLOPs']:.0f} TFLOP/s; "
             f"fused is {u['fused_speedup']:.2f}x faster")
         extra["prefill_unfused_bf16"] = u
+        if args.cpu_budget > 0:
+            log("timing the fp64 prefill oracle on a sample ...")
+            cpu_other["prefill_bf16"] = cpu_prefill_sample(torch, wl, pc)
+            log(f"  prefill oracle: {cpu_other['prefill_bf16']['value']:.2f} GFLOP/s")
         del pc
         torch.cuda.empty_cache()
         log("generating copy_bf16 ...")
@@ -544,6 +599,9 @@ def main() -> int:
         r = bench_copy(pa, torch, wl, cc, args.steps, args.warmup)
         log(f"  copy: {r['kernel_ms']:.3f} ms, {r['kernel_GBps']:.0f} GB/s")
         extra["copy_bf16"] = r
+        if args.cpu_budget > 0:
+            cpu_other["copy_bf16"] = cpu_copy_sample(torch, wl, cc)
+            log(f"  copy oracle: {cpu_other['copy_bf16']['value']:.2f} GB/s")
         del cc
         torch.cuda.empty_cache()
         log("generating append_bf16 ...")
@@ -602,6 +660,7 @@ def main() -> int:
             "kernel_ms": round(res["kernel_ms"], 5), "bytes_per_launch": res["bytes"],
         },
         "cpu_baseline": cpu,
+        "cpu_oracle_other": cpu_other or None,
         "tokens_per_s": round(res["tokens_per_s"], 1),
         "extra": extra,
     }
