@@ -201,7 +201,9 @@ pa_status_t paged_attn_prefill(void *out, const void *query, const void *k_cache
  * when the matrix library finds no kernel for a shape).  The first call on a
  * device creates a hipBLASLt handle there, which lives until the process
  * ends; a failure to create it is PA_ERR_DEVICE.  Work is enqueued on
- * `stream` one sequence after another.
+ * `stream` one sequence after another; if an error is returned after the
+ * first sequence was enqueued, the rows of the earlier sequences may already
+ * be written.
  * ------------------------------------------------------------------------ */
 size_t paged_attn_prefill_unfused_workspace_size(int32_t max_query_len, int32_t max_context_len,
                                                  int32_t num_heads, int32_t num_kv_heads,
