@@ -28,7 +28,8 @@
 //     sharing a SIMD keep both busy;
 //   * K and V tiles go from the paged cache straight into LDS
 //     (global_load_lds_dwordx4, no registers, no LDS write instructions), four
-//     stages each, issued by the matrix group between its MFMAs; completion is
+//     stages each, issued by the matrix group between its MFMAs (after the
+//     first half of QK^T); completion is
 //     awaited with exact vmcnt counts before the barrier that publishes a
 //     tile, so loads of the next tiles stay in flight across phases;
 //   * per 64-key tile a wavefront computes S^T = K Q^T (2 x D/16 MFMA
@@ -506,9 +507,12 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
       const bool qk = j < wave_tiles;
       const bool pv = j >= 1 && j - 1 < wave_tiles;
       const int lt = GRP == 0 ? j + NS - 1 : j + NS - 2;     // tile loaded this step
+      // All of this step's tile loads go out after the first 32-key half of
+      // QK^T (same-box A/B: 2.2% faster than half after each QK half, and
+      // ahead of issuing them at the phase start, after the first four MFMAs
+      // or after the second half).
       auto between = [&](int kt) {
-        if (kt == 0) load_tile(lt, ids, 0, IPW / 2);
-        else load_tile(lt, ids, IPW / 2, IPW);
+        if (kt == 0) load_tile(lt, ids, 0, IPW);
       };
       // The wavefront in its matrix phase runs at raised issue priority, so
       // that its operand reads and MFMAs win the SIMD's arbitration against
