@@ -26,7 +26,7 @@ __all__ = [
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 DEFAULT_PARTITION = 512       # PA_DEFAULT_PARTITION
-DEFAULT_PARTITION_GQA = 1024  # PA_DEFAULT_PARTITION_GQA
+DEFAULT_PARTITION_GQA = 2048  # PA_DEFAULT_PARTITION_GQA
 
 
 def default_partition(num_heads: int, num_kv_heads: int) -> int:
