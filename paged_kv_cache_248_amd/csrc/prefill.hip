@@ -40,8 +40,8 @@
 //     k-step is permuted identically in both operands, so no shuffle is needed;
 //   * K and V are row-major in LDS with XOR swizzles of the 16-byte chunks;
 //     the V^T operand is read with the transposing ds_read_b64_tr_b16; the
-//     operand reads of the next group of four MFMAs are in flight while the
-//     current four execute;
+//     operand reads of the seven MFMAs after the current one are in flight
+//     while it executes;
 //   * the grid is persistent (one work-group per CU, each taking several
 //     work items), which removes the idle time between one work-group's end
 //     and the next one's start on a CU; the item order is XCD-aware: the
@@ -63,7 +63,7 @@ constexpr int kBN = 64;        // keys per tile
 constexpr int kRows = 32;      // query rows per wavefront
 constexpr int kWaves = 8;      // two groups of four
 constexpr int kStages = 4;     // LDS stages per K and per V tile stream
-constexpr int kReadAhead = 1;  // MFMA operand units whose LDS reads are in flight
+constexpr int kReadAhead = 7;  // MFMAs whose operand reads are in flight ahead of the current one
 constexpr int kXcds = 8;       // XCDs of an MI355X; work-group ids are dealt to them round-robin
 
 struct PrefillParams {
@@ -350,71 +350,63 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
     constexpr int QU = KS / 4 * 2;                // QK units
     constexpr int U = QU + DT;                    // all units
     auto matrix_phase = [&](uint32_t kb, uint32_t vb, bool do_pv, auto &&between) {
+      // One unit = one MFMA; the operand reads of unit u + AHEAD are issued
+      // before the MFMA of unit u (same-box A/B: 7 ahead, one MFMA per unit,
+      // +0.9% over groups of four MFMAs read one group ahead; 5 ahead +0.7%;
+      // 9 ahead runs out of registers and loses 1.3%).
       constexpr int AHEAD = kReadAhead;
-      u32x4 R[AHEAD + 1][4];
+      constexpr int QN = 2 * KS;                  // QK MFMAs, (kt, ks) with kt major
+      constexpr int PN = 4 * DT;                  // PV MFMAs, (dt, ks2) with dt major
+      u32x4 R[AHEAD + 1];
       auto issue = [&](auto u_tag) {
         constexpr int u = decltype(u_tag)::value;
-        u32x4(&r)[4] = R[u % (AHEAD + 1)];
-        if constexpr (u < QU) {
-          constexpr int kt = u / (KS / 4), ks0 = 4 * (u % (KS / 4));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) r[i] = lds_b128<kt * 32 * ROWB>(kb + k_rd[ks0 + i]);
+        u32x4 &r = R[u % (AHEAD + 1)];
+        if constexpr (u < QN) {
+          constexpr int kt = u / KS, ks = u % KS;
+          r = lds_b128<kt * 32 * ROWB>(kb + k_rd[ks]);
         } else {
-          constexpr int dt = u - QU;
-          const uint32_t a = vb + v_tr[dt];
-          // keys 16 ks2 + 4h + 0..3 and 16 ks2 + 8 + 4h + 0..3 of the tile
-          const u32x2 l0 = lds_tr16<0 * ROWB>(a), h0 = lds_tr16<8 * ROWB>(a);
-          const u32x2 l1 = lds_tr16<16 * ROWB>(a), h1 = lds_tr16<24 * ROWB>(a);
-          const u32x2 l2 = lds_tr16<32 * ROWB>(a), h2 = lds_tr16<40 * ROWB>(a);
-          const u32x2 l3 = lds_tr16<48 * ROWB>(a), h3 = lds_tr16<56 * ROWB>(a);
-          r[0] = u32x4{l0[0], l0[1], h0[0], h0[1]};
-          r[1] = u32x4{l1[0], l1[1], h1[0], h1[1]};
-          r[2] = u32x4{l2[0], l2[1], h2[0], h2[1]};
-          r[3] = u32x4{l3[0], l3[1], h3[0], h3[1]};
+          constexpr int dt = (u - QN) / 4, ks2 = (u - QN) % 4;
+          const uint32_t ad = vb + v_tr[dt];
+          const u32x2 lo = lds_tr16<(16 * ks2) * ROWB>(ad), hi = lds_tr16<(16 * ks2 + 8) * ROWB>(ad);
+          r = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
       };
       auto consume = [&](auto u_tag) {
         constexpr int u = decltype(u_tag)::value;
-        u32x4(&r)[4] = R[u % (AHEAD + 1)];
-        if constexpr (u < QU) {
-          constexpr int kt = u / (KS / 4), ks0 = 4 * (u % (KS / 4));
-          f32x16 acc = ks0 == 0 ? f32x16{} : s[kt];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc = mfma32<E>(r[i], qf[ks0 + i], acc);
-          s[kt] = acc;
+        u32x4 &r = R[u % (AHEAD + 1)];
+        if constexpr (u < QN) {
+          constexpr int kt = u / KS, ks = u % KS;
+          s[kt] = mfma32<E>(r, qf[ks], ks == 0 ? f32x16{} : s[kt]);
         } else {
-          constexpr int dt = u - QU;
-#pragma unroll
-          for (int ks2 = 0; ks2 < 4; ++ks2) o[dt] = mfma32<E>(r[ks2], pf[ks2], o[dt]);
+          constexpr int dt = (u - QN) / 4, ks2 = (u - QN) % 4;
+          o[dt] = mfma32<E>(r, pf[ks2], o[dt]);
         }
       };
       auto pipeline = [&](auto n_tag) {
-        constexpr int N = decltype(n_tag)::value;   // units run: QU (QK only) or U
-        // LDS reads of a unit: 4 (K) or 8 (V^T halves)
-        constexpr auto ops = [](int v) { return v < QU ? 4 : 8; };
+        constexpr int N = decltype(n_tag)::value;   // units run: QN (QK only) or QN + PN
+        constexpr auto ops = [](int v) { return v < QN ? 1 : 2; };
         for_each_index(std::make_integer_sequence<int, (AHEAD < N ? AHEAD : N)>{},
                        [&](auto u_tag) { issue(u_tag); });
         for_each_index(std::make_integer_sequence<int, N>{}, [&](auto u_tag) {
             constexpr int u = decltype(u_tag)::value;
             if constexpr (u + AHEAD < N) issue(std::integral_constant<int, u + AHEAD>{});
-            // reads issued after unit u's: those of units u+1 .. min(u+AHEAD, N-1)
             constexpr int later = [&] {
               int n = 0;
               for (int v = u + 1; v <= u + AHEAD && v < N; ++v) n += ops(v);
               return n;
             }();
-            // (lgkmcnt holds at most 15: waiting for fewer is only stricter)
-            lds_tie<(later < 15 ? later : 15)>(R[u % (AHEAD + 1)]);
+            asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(R[u % (AHEAD + 1)]) : "i"(later < 15 ? later : 15));
             consume(std::integral_constant<int, u>{});
-            if constexpr (u < QU && (u + 1) % (KS / 4) == 0) {
+            if constexpr (u == KS - 1) {
               __builtin_amdgcn_sched_barrier(0);
-              between(u / (KS / 4));
+              between(0);
               __builtin_amdgcn_sched_barrier(0);
             }
         });
       };
-      if (do_pv) pipeline(std::integral_constant<int, U>{});
-      else pipeline(std::integral_constant<int, QU>{});
+      (void)U;
+      if (do_pv) pipeline(std::integral_constant<int, QN + PN>{});
+      else pipeline(std::integral_constant<int, QN>{});
     };
 
     // Softmax of tile j's scores: online update of (m, l, O) and the P^T
