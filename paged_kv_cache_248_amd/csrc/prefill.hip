@@ -29,7 +29,7 @@
 //   * K and V tiles go from the paged cache straight into LDS
 //     (global_load_lds_dwordx4, no registers, no LDS write instructions), four
 //     stages each, issued by the matrix group between its MFMAs (after the
-//     first half of QK^T); completion is
+//     first quarter of QK^T); completion is
 //     awaited with exact vmcnt counts before the barrier that publishes a
 //     tile, so loads of the next tiles stay in flight across phases;
 //   * per 64-key tile a wavefront computes S^T = K Q^T (2 x D/16 MFMA
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
             }();
             asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(R[u % (AHEAD + 1)]) : "i"(later < 15 ? later : 15));
             consume(std::integral_constant<int, u>{});
-            if constexpr (u == KS - 1) {
+            if constexpr (u == KS / 2 - 1) {
               __builtin_amdgcn_sched_barrier(0);
               between(0);
               __builtin_amdgcn_sched_barrier(0);
@@ -499,10 +499,11 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
       const bool qk = j < wave_tiles;
       const bool pv = j >= 1 && j - 1 < wave_tiles;
       const int lt = GRP == 0 ? j + NS - 1 : j + NS - 2;     // tile loaded this step
-      // All of this step's tile loads go out after the first 32-key half of
-      // QK^T (same-box A/B: 2.2% faster than half after each QK half, and
-      // ahead of issuing them at the phase start, after the first four MFMAs
-      // or after the second half).
+      // All of this step's tile loads go out after the first quarter of the
+      // QK^T MFMAs (four for head_dim 128).  Same-box A/B runs: issuing them
+      // all at one point beat splitting them over the two QK halves by 2.2%;
+      // of the points tried (phase start, after 2, 4, 6, 8 or 12 of the 16
+      // QK MFMAs) after 4 was fastest, 0.4% ahead of 2, 6 and 8.
       auto between = [&](int kt) {
         if (kt == 0) load_tile(lt, ids, 0, IPW);
       };
