@@ -158,3 +158,22 @@ def test_prefill_workload_full_size_sampled():
         got = host(out[int(qsl[b]):int(qsl[b + 1])])
         e = assert_close(got[rows][:, heads], ref[rows][:, heads], "bf16", f"seq {b}")
         log(f"  seq {b} (ctx {ctx[b]}): {len(rows)} rows x {len(heads)} heads, max rel err {e:.3e}")
+
+
+@pytest.mark.parametrize("dtype,bs", [("bf16", 32), ("f16", 16), ("bf16", 8)])
+def test_prefill_long_context(dtype, bs):
+    """Contexts of 32768 and 20000 keys (prefixes of 32568 and 19900 tokens):
+    page indices and key offsets at the top of the supported range, several
+    hundred key tiles per query tile; sampled rows against the oracle."""
+    pre = np.array([32768 - 200, 20000 - 100])
+    ql = np.array([200, 100])
+    case = wl.make_prefill(pre, ql, 8, 2, 128, bs, dtype, seed=41 + bs, device=DEV, poison=True)
+    kv = case.kv
+    out = run_prefill(case)
+    assert torch.isfinite(out.float()).all()
+    rows = np.array([0, 1, 63, 64, 127, 199, 200, 201, 263, 299])
+    ref = prefill_ref(host(case.query), host(kv.k_cache), host(kv.v_cache),
+                      host(kv.block_tables), host(kv.context_lens),
+                      host(case.query_start_loc), case.scale, rows=rows)
+    e = assert_close(host(out)[rows], ref[rows], dtype, "long-context prefill")
+    log(f"long-context prefill {dtype} bs={bs}: max rel err {e:.3e}")
