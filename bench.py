@@ -239,6 +239,46 @@ def bench_tiny_decode(pa, torch, wl, steps, warmup):
             "context_lens": ctx.tolist(), "steps": steps, "warmup": warmup}
 
 
+def bench_block_manager(pa, wl, steps: int = 200):
+    """Host bookkeeping of one decode step (one more token for each of 256
+    requests, then the kernels' block tables for the batch) in the native
+    block manager, and the same with the Python oracle (the baseline).
+    Requests start from lognormal prompts (median 2048, sigma 1), 16-token
+    blocks, the pool sized to the prompts plus room for every appended token."""
+    from oracle.block_manager_oracle import BlockManagerOracle
+    rng = np.random.default_rng(2486)
+    n_req, bs = 256, 16
+    prompts = np.clip(np.round(2048 * np.exp(rng.standard_normal(n_req))), 16, 32768).astype(int)
+    pool = int(sum((p + steps + bs - 1) // bs for p in prompts) * 1.1)
+    ids = list(range(n_req))
+    mbps = int(max((p + steps + bs - 1) // bs for p in prompts))
+    bm = pa.BlockManager(pool, bs)
+    ref = BlockManagerOracle(pool, bs)
+    for i, p in enumerate(prompts):
+        bm.register(i, int(p))
+        ref.register(i, int(p))
+    import torch
+    out = (torch.empty((n_req, mbps), dtype=torch.int32), torch.empty(n_req, dtype=torch.int32))
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        bm.append_tokens(ids)
+        bm.batch_tables(ids, mbps, out=out)
+    native_us = (time.perf_counter() - t0) * 1e6 / steps
+    ref_steps = max(1, steps // 10)
+    t0 = time.perf_counter()
+    for _ in range(ref_steps):
+        for i in ids:
+            ref.append_token(i)
+        tables = np.full((n_req, mbps), -1, dtype=np.int32)
+        for i in ids:
+            tables[i, :len(ref.tables[i])] = ref.tables[i]
+        lens = np.array([ref.tokens[i] for i in ids], dtype=np.int32)
+    oracle_us = (time.perf_counter() - t0) * 1e6 / ref_steps
+    return {"workload": "block_manager_decode_step", "requests": n_req, "block_size": bs,
+            "pool_blocks": pool, "native_us_per_step": native_us,
+            "oracle_us_per_step": oracle_us, "steps": steps, "oracle_steps": ref_steps}
+
+
 def bench_copy(pa, torch, wl, case, steps, warmup):
     n = wl.copy_count_unique(case.src_to_dst.cpu().numpy(), case.src_k.shape[0],
                              case.dst_k.shape[0])
@@ -498,7 +538,7 @@ def main() -> int:
                                                        "long_decode_f16", "prefill_bf16",
                                                        "copy_bf16", "append_bf16", "swap_bf16",
                                                        "stream_copy", "stream_read", "prefill_unfused_bf16",
-                                                       "tiny_decode_f32"],
+                                                       "tiny_decode_f32", "block_manager"],
                     help="run one workload, print its result object and exit (profiling)")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
@@ -525,6 +565,9 @@ def main() -> int:
 
     if args.only == "stream_copy":
         print(json.dumps(bench_stream_copy(torch, args.steps, args.warmup)), flush=True)
+        return 0
+    if args.only == "block_manager":
+        print(json.dumps(bench_block_manager(pa, wl)), flush=True)
         return 0
     if args.only == "tiny_decode_f32":
         print(json.dumps(bench_tiny_decode(pa, torch, wl, args.steps, args.warmup)), flush=True)
@@ -619,6 +662,10 @@ def main() -> int:
         extra["swap_bf16"] = r
         del sc
         torch.cuda.empty_cache()
+        r = bench_block_manager(pa, wl)
+        log(f"  block manager decode step (256 requests): {r['native_us_per_step']:.1f} us native, "
+            f"{r['oracle_us_per_step']:.0f} us oracle")
+        extra["block_manager"] = r
         r = bench_stream_read(pa, torch, min(args.steps, 50), min(args.warmup, 20))
         log(f"  plain read stream: {r['GBps']:.0f} GB/s")
         extra["stream_read"] = r

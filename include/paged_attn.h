@@ -322,6 +322,13 @@ pa_status_t paged_kv_append(void *k_cache, void *v_cache, const void *key, const
  *                     copy the block's K and V (paged_kv_copy_blocks); else
  *                     both receive -1.  PA_ERR_NO_BLOCKS leaves the request
  *                     unchanged
+ *   pa_bm_append_tokens  one decode step: one more token for each of the
+ *                     num_requests listed requests, in list order, exactly
+ *                     as that many pa_bm_append_token calls; cow_src[i] /
+ *                     cow_dst[i] (arrays of num_requests, may be NULL)
+ *                     receive request i's pair.  All or nothing: an unknown
+ *                     or repeated id (PA_ERR_REQUEST) or too few free blocks
+ *                     for the whole batch (PA_ERR_NO_BLOCKS) changes nothing
  *   pa_bm_fork        child_id shares every block of parent_id (each count
  *                     + 1) and starts with its token count (prefix sharing)
  *   pa_bm_finish      releases every block of the request and forgets it
@@ -344,6 +351,8 @@ void pa_bm_destroy(pa_block_manager *bm);
 pa_status_t pa_bm_register(pa_block_manager *bm, int64_t request_id, int64_t prompt_len);
 pa_status_t pa_bm_append_token(pa_block_manager *bm, int64_t request_id, int32_t *cow_src,
                                int32_t *cow_dst);
+pa_status_t pa_bm_append_tokens(pa_block_manager *bm, const int64_t *request_ids,
+                                int32_t num_requests, int32_t *cow_src, int32_t *cow_dst);
 pa_status_t pa_bm_fork(pa_block_manager *bm, int64_t parent_id, int64_t child_id);
 pa_status_t pa_bm_finish(pa_block_manager *bm, int64_t request_id);
 int32_t pa_bm_free_count(const pa_block_manager *bm);

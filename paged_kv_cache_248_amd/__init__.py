@@ -62,6 +62,7 @@ _SIGS = {
     "pa_bm_destroy": (None, [_VP]),
     "pa_bm_register": (ctypes.c_int, [_VP, _I64, _I64]),
     "pa_bm_append_token": (ctypes.c_int, [_VP, _I64, ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
+    "pa_bm_append_tokens": (ctypes.c_int, [_VP, _VP, _I32, _VP, _VP]),
     "pa_bm_fork": (ctypes.c_int, [_VP, _I64, _I64]),
     "pa_bm_finish": (ctypes.c_int, [_VP, _I64]),
     "pa_bm_free_count": (_I32, [_VP]),
@@ -442,6 +443,20 @@ class BlockManager:
                                               ctypes.byref(b)), "append_token")
         return None if a.value < 0 else (a.value, b.value)
 
+    def append_tokens(self, request_ids):
+        """One more token for each listed request, in order (one decode step),
+        all or nothing.  Returns (cow_src, cow_dst) int32 arrays with the
+        copy-on-write pair of each request, -1 where none."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(request_ids, dtype=np.int64))
+        src = np.empty(ids.size, dtype=np.int32)
+        dst = np.empty(ids.size, dtype=np.int32)
+        self._st(self._lib.pa_bm_append_tokens(self._h, ids.ctypes.data_as(ctypes.c_void_p),
+                                               int(ids.size), src.ctypes.data_as(ctypes.c_void_p),
+                                               dst.ctypes.data_as(ctypes.c_void_p)),
+                 "append_tokens")
+        return src, dst
+
     def fork(self, parent_id: int, child_id: int) -> None:
         self._st(self._lib.pa_bm_fork(self._h, int(parent_id), int(child_id)), "fork")
 
@@ -483,13 +498,23 @@ class BlockManager:
         self._st(self._lib.pa_bm_ref_count(self._h, int(block), ctypes.byref(c)), "ref_count")
         return int(c.value)
 
-    def batch_tables(self, request_ids, max_blocks_per_seq: int):
+    def batch_tables(self, request_ids, max_blocks_per_seq: int, out=None):
         """(block_tables int32 [n, max_blocks_per_seq] with -1 padding,
-        context_lens int32 [n]) for the kernels, as CPU tensors."""
+        context_lens int32 [n]) for the kernels, as CPU tensors; ``out`` may
+        pass a (tables, lens) pair of contiguous CPU int32 tensors to reuse."""
         ids = torch.as_tensor(list(request_ids), dtype=torch.int64)
         n = ids.numel()
-        tables = torch.empty((n, int(max_blocks_per_seq)), dtype=torch.int32)
-        lens = torch.empty(n, dtype=torch.int32)
+        if out is None:
+            tables = torch.empty((n, int(max_blocks_per_seq)), dtype=torch.int32)
+            lens = torch.empty(n, dtype=torch.int32)
+        else:
+            tables, lens = out
+            if (tables.dtype != torch.int32 or lens.dtype != torch.int32 or tables.is_cuda
+                    or lens.is_cuda or not tables.is_contiguous() or not lens.is_contiguous()
+                    or tuple(tables.shape) != (n, int(max_blocks_per_seq))
+                    or tuple(lens.shape) != (n,)):
+                raise ValueError("out must be contiguous CPU int32 tensors of shapes "
+                                 "[n, max_blocks_per_seq] and [n]")
         self._st(self._lib.pa_bm_fill_batch(self._h, ctypes.c_void_p(ids.data_ptr()), n,
                                             int(max_blocks_per_seq),
                                             ctypes.c_void_p(tables.data_ptr()),

@@ -15,6 +15,7 @@
 // re-sort on release); tables are vectors in a hash map keyed by request id.
 // Every operation checks before it changes anything, so a failure leaves
 // the manager as it was.
+#include <algorithm>
 #include <cstdint>
 #include <new>
 #include <set>
@@ -104,6 +105,42 @@ pa_status_t pa_bm_append_token(pa_block_manager *bm, int64_t request_id, int32_t
   return PA_OK;
 }
 
+pa_status_t pa_bm_append_tokens(pa_block_manager *bm, const int64_t *request_ids,
+                                int32_t num_requests, int32_t *cow_src, int32_t *cow_dst) {
+  if (!bm) return PA_ERR_NULL;
+  if (num_requests < 0) return PA_ERR_SHAPE;
+  if (num_requests == 0) return PA_OK;
+  if (!request_ids) return PA_ERR_NULL;
+  // Check the whole batch first: every id known and listed once, and enough
+  // free blocks for the appends in list order (a copy-on-write lowers the
+  // count of the shared block, which a later request of the batch may share).
+  std::unordered_map<int64_t, char> seen;
+  std::unordered_map<int32_t, int32_t> dropped;     // block -> references given up so far
+  seen.reserve((size_t)num_requests);
+  int64_t need = 0;
+  for (int32_t i = 0; i < num_requests; ++i) {
+    auto it = bm->requests.find(request_ids[i]);
+    if (it == bm->requests.end() || !seen.emplace(request_ids[i], 1).second) return PA_ERR_REQUEST;
+    const pa_block_manager::Request &r = it->second;
+    if (r.tokens % bm->block_size == 0) {
+      ++need;
+    } else {
+      const int32_t last = r.blocks.back();
+      auto d = dropped.find(last);
+      const int32_t refs = bm->ref[last] - (d == dropped.end() ? 0 : d->second);
+      if (refs > 1) {
+        ++need;
+        ++dropped[last];
+      }
+    }
+  }
+  if (need > (int64_t)bm->free_ids.size()) return PA_ERR_NO_BLOCKS;
+  for (int32_t i = 0; i < num_requests; ++i)
+    (void)pa_bm_append_token(bm, request_ids[i], cow_src ? cow_src + i : nullptr,
+                             cow_dst ? cow_dst + i : nullptr);
+  return PA_OK;
+}
+
 pa_status_t pa_bm_fork(pa_block_manager *bm, int64_t parent_id, int64_t child_id) {
   if (!bm) return PA_ERR_NULL;
   auto it = bm->requests.find(parent_id);
@@ -176,8 +213,8 @@ pa_status_t pa_bm_fill_batch(const pa_block_manager *bm, const int64_t *request_
   for (int32_t i = 0; i < num_requests; ++i) {
     const auto &r = bm->requests.find(request_ids[i])->second;
     int32_t *row = block_tables + (size_t)i * max_blocks_per_seq;
-    for (int32_t j = 0; j < max_blocks_per_seq; ++j)
-      row[j] = j < (int32_t)r.blocks.size() ? r.blocks[j] : -1;
+    std::copy(r.blocks.begin(), r.blocks.end(), row);
+    std::fill(row + r.blocks.size(), row + max_blocks_per_seq, -1);
     context_lens[i] = (int32_t)r.tokens;
   }
   return PA_OK;

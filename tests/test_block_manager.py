@@ -125,3 +125,87 @@ def test_create_rejects_bad_sizes():
         pa.BlockManager(0, 16)
     with pytest.raises(pa.PagedAttnError):
         pa.BlockManager(8, 0)
+
+
+def oracle_batch(ref, ids):
+    """The batch as its definition: the appends one by one, in list order,
+    and nothing kept if any of them fails (run on a copy, then adopted)."""
+    import copy
+    trial = copy.deepcopy(ref)
+    if len(set(ids)) != len(ids) or any(i not in trial.tables for i in ids):
+        raise KeyError("unknown or repeated request")
+    pairs = [trial.append_token(i) for i in ids]     # OutOfBlocks propagates
+    ref.__dict__.update(trial.__dict__)
+    return pairs
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_batch_append_matches_single_appends(seed):
+    """Random decode steps over requests that share blocks (forks): the
+    native batch gives the same copy-on-write pairs and the same state as
+    the appends one at a time, and a batch that cannot be served whole
+    changes nothing."""
+    rng = np.random.default_rng(5000 + seed)
+    nblocks, bs = int(rng.integers(8, 60)), int(rng.choice([1, 2, 4, 16]))
+    bm, ref = pa.BlockManager(nblocks, bs), BlockManagerOracle(nblocks, bs)
+    live, next_id = [], 0
+    for _ in range(120):
+        op = int(rng.integers(0, 10))
+        if op < 2 or not live:
+            args = (next_id, int(rng.integers(0, 2 * bs + 2)))
+            try:
+                ref.register(*args)
+                bm.register(*args)
+                live.append(next_id)
+            except OutOfBlocks:
+                with pytest.raises(pa.OutOfBlocksError):
+                    bm.register(*args)
+            next_id += 1
+        elif op < 4:
+            parent = int(rng.choice(live))
+            ref.fork(parent, next_id)
+            bm.fork(parent, next_id)
+            live.append(next_id)
+            next_id += 1
+        elif op < 5 and len(live) > 1:
+            rid = int(rng.choice(live))
+            ref.finish(rid)
+            bm.finish(rid)
+            live.remove(rid)
+        else:
+            k = int(rng.integers(1, len(live) + 1))
+            ids = [int(x) for x in rng.choice(live, size=k, replace=False)]
+            if rng.random() < 0.1:
+                ids.append(ids[0])                       # a repeated id: refused whole
+            try:
+                want = oracle_batch(ref, ids)
+            except KeyError:
+                with pytest.raises(pa.PagedAttnError):
+                    bm.append_tokens(ids)
+                same_state(bm, ref, live)
+                continue
+            except OutOfBlocks:
+                with pytest.raises(pa.OutOfBlocksError):
+                    bm.append_tokens(ids)
+                same_state(bm, ref, live)
+                continue
+            src, dst = bm.append_tokens(ids)
+            got = [None if s < 0 else (int(s), int(d)) for s, d in zip(src, dst)]
+            assert got == want
+        same_state(bm, ref, live)
+
+
+def test_batch_append_shared_block_copies_once_per_sharer():
+    bm = pa.BlockManager(8, 4)
+    bm.register(1, 6)                   # blocks 0, 1 (block 1 partly filled)
+    bm.fork(1, 2)
+    bm.fork(1, 3)                       # block 1 shared three ways
+    src, dst = bm.append_tokens([1, 2, 3])
+    # the first two sharers copy; the third is then the only holder
+    assert src.tolist() == [1, 1, -1] and dst.tolist() == [2, 3, -1]
+    assert bm.table(3) == [0, 1] and bm.ref_count(1) == 1
+    with pytest.raises(pa.PagedAttnError):
+        bm.append_tokens([1, 99])
+    with pytest.raises(pa.PagedAttnError):
+        bm.append_tokens([1, 1])
+    assert [bm.tokens(r) for r in (1, 2, 3)] == [7, 7, 7]
