@@ -4,9 +4,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
-#include <mutex>
 
 #include "../../include/paged_attn.h"
 #include "pa_internal.h"
@@ -14,17 +14,18 @@
 namespace pa {
 
 int device_cu_count() {
-  static std::mutex mu;
-  static int cache[64] = {};
+  static std::atomic<int> cache[64];   // per device; 0 = not queried yet
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     cus = 256;
-  std::lock_guard<std::mutex> lk(mu);
-  if (dev < 64) cache[dev] = cus;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 

@@ -40,6 +40,8 @@
 //     id -> data dependency never drains the K/V pipeline;
 //   * reductions only depend on a token's logical position, never on its
 //     physical block, so permuting the pool leaves results bit-identical.
+#include <atomic>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -880,12 +882,15 @@ hipError_t launch_typed(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStr
     if constexpr (MF) return decode_mfma_kernel<E, D, GT>;
     else return decode_kernel<E, D, GT>;
   }();
-  static int occ = 0;   // per instantiation
+  static std::atomic<int> occ_cache[64];   // per instantiation and device; 0 = not queried
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  const bool cached = dev >= 0 && dev < 64;
+  int occ = cached ? occ_cache[dev].load(std::memory_order_relaxed) : 0;
   if (occ == 0) {
-    int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kernel, 256, 0) != hipSuccess || o < 1)
-      o = 2;
-    occ = o;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 256, 0) != hipSuccess || occ < 1)
+      occ = 2;
+    if (cached) occ_cache[dev].store(occ, std::memory_order_relaxed);
   }
   const long long upper =
       (long long)a.num_seqs * a.max_parts * a.num_kv_heads * p.head_chunks;

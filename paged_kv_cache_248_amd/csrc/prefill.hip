@@ -49,6 +49,7 @@
 //     through all its query tiles (the last, with the most keys, first), so
 //     the tiles sharing K/V run together in one L2.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -607,9 +608,8 @@ hipError_t launch_typed(const PrefillLaunch &a, hipStream_t stream) {
   // Items of the XCD with the most; one work-group per CU at most.
   const long long xcd_items = ((pairs + kXcds - 1) / kXcds) * qtiles;
   if (xcd_items > 0x7fffffffLL) return hipErrorInvalidValue;
-  int cus = 0;
+  int cus = 0, dev = 0;
   {
-    int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
@@ -618,13 +618,17 @@ hipError_t launch_typed(const PrefillLaunch &a, hipStream_t stream) {
   p.num_pairs = (int32_t)pairs;
   p.num_qtiles = (int32_t)qtiles;
   const size_t lds_bytes = (size_t)2 * kStages * 64 * D * 2;
-  static bool attr_set = false;   // per instantiation; the attribute is per function
-  if (!attr_set) {
+  // The LDS attribute belongs to the function on one device: bit d of this
+  // per-instantiation mask records that device d has it (devices past 63 set
+  // it on every call).
+  static std::atomic<uint64_t> attr_devices{0};
+  const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t{1} << dev : 0;
+  if (bit == 0 || (attr_devices.load(std::memory_order_relaxed) & bit) == 0) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_kernel<E, D>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)lds_bytes);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_devices.fetch_or(bit, std::memory_order_relaxed);
   }
   profile_begin(stream);
   hipLaunchKernelGGL((prefill_kernel<E, D>), dim3((unsigned)grid), dim3(64 * kWaves), lds_bytes,
