@@ -1,0 +1,156 @@
+"""Entry points captured into HIP graphs (a serving loop records one step and
+replays it).  The library records no memset nodes, and every launch reads its
+inputs through the pointers captured, so each replay must equal the eager
+call on the inputs of that moment bit for bit.  Each test writes new input
+values between replays and runs eager work in between."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_248_amd as pa
+import workloads as wl
+from oracle import copy_blocks_ref, decode_ref, prefill_ref
+from tests._util import assert_close, host, log
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+REPLAYS = 3
+
+
+def bits(t: torch.Tensor) -> torch.Tensor:
+    return t.view({4: torch.int32, 2: torch.int16}[t.element_size()])
+
+
+def capture(fn):
+    fn()                                   # first call outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def refill(t: torch.Tensor, gen: torch.Generator) -> None:
+    t.copy_(torch.randn(t.shape, generator=gen).to(t.dtype).to(DEV))
+
+
+def test_split_gqa_decode_graph_replays_match_eager():
+    """bf16 GQA decode split into 256-token partitions: plan, matrix-core
+    attention and merge launches in one graph."""
+    case = wl.make_decode([3, 513, 1500, 90, 1100], 32, 8, 128, 16, "bf16", seed=41, device=DEV)
+    kv = case.kv
+    B, Hq, D = case.query.shape
+    maxctx = kv.max_context_len
+    size = max(1, pa.paged_attn_decode_workspace_size(B, Hq, kv.k_cache.shape[1], D, maxctx, 256))
+    ws = torch.empty(size, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(case.query)
+
+    def call(o, w):
+        pa.paged_attn_decode(o, case.query, kv.k_cache, kv.v_cache, kv.block_tables,
+                             kv.context_lens, case.scale, maxctx, partition_size=256,
+                             workspace=w)
+
+    g = capture(lambda: call(out, ws))
+    gen = torch.Generator(device="cpu").manual_seed(41)
+    eager_out, eager_ws = torch.empty_like(out), torch.empty_like(ws)
+    for r in range(REPLAYS):
+        refill(case.query, gen)
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        call(eager_out, eager_ws)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(out), bits(eager_out)), f"replay {r}"
+    ref = decode_ref(host(case.query), host(kv.k_cache), host(kv.v_cache), host(kv.block_tables),
+                     host(kv.context_lens), case.scale)
+    assert_close(host(out), ref, "bf16", "split decode graph")
+    log(f"split GQA decode: {REPLAYS} replays bit-identical to eager")
+
+
+def test_prefill_graph_replays_match_eager():
+    case = wl.make_prefill([0, 200, 35], [130, 64, 7], 16, 4, 128, 16, "bf16", seed=42,
+                           device=DEV)
+    kv = case.kv
+    maxq, maxctx = case.max_query_len, kv.max_context_len
+    out = torch.empty_like(case.query)
+
+    def call(o):
+        pa.paged_attn_prefill(o, case.query, kv.k_cache, kv.v_cache, kv.block_tables,
+                              kv.context_lens, case.query_start_loc, case.scale, maxq, maxctx)
+
+    g = capture(lambda: call(out))
+    gen = torch.Generator(device="cpu").manual_seed(42)
+    eager_out = torch.empty_like(out)
+    for r in range(REPLAYS):
+        refill(case.query, gen)
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        call(eager_out)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(out), bits(eager_out)), f"replay {r}"
+    ref = prefill_ref(host(case.query), host(kv.k_cache), host(kv.v_cache),
+                      host(kv.block_tables), host(kv.context_lens), host(case.query_start_loc),
+                      case.scale)
+    assert_close(host(out), ref, "bf16", "prefill graph")
+
+
+def test_append_graph_replays_match_eager():
+    case = wl.make_append([10, 0, 40], [7, 20, 3], 2, 128, 16, "bf16", seed=43, device=DEV)
+    kv = case.kv
+    k2, v2 = kv.k_cache.clone(), kv.v_cache.clone()
+
+    def call(kc, vc):
+        pa.paged_kv_append(kc, vc, case.key, case.value, kv.block_tables, kv.context_lens,
+                           case.query_start_loc)
+
+    g = capture(lambda: call(kv.k_cache, kv.v_cache))
+    call(k2, v2)                           # the eager pools saw the same two calls
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cpu").manual_seed(43)
+    for r in range(REPLAYS):
+        refill(case.key, gen)
+        refill(case.value, gen)
+        g.replay()
+        torch.cuda.synchronize()
+        call(k2, v2)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(kv.k_cache), bits(k2)), f"replay {r}: K pool"
+        assert torch.equal(bits(kv.v_cache), bits(v2)), f"replay {r}: V pool"
+
+
+def test_copy_blocks_graph_replays_match_eager():
+    """Block copy (fill, resolve and copy launches) in one graph, with its
+    workspace passed in; repeated destinations resolve to the lowest source."""
+    mapping = np.array([3, -1, 7, 3, 0, 11, 7, 2, -1, 5, 9, 1], dtype=np.int64)
+    case = wl.make_copy(len(mapping), 12, (2, 16, 128), "bf16", seed=44, device=DEV,
+                        mapping=mapping)
+    ws = torch.empty(max(1, pa.paged_kv_copy_blocks_workspace_size(case.dst_k.shape[0])),
+                     dtype=torch.uint8, device=DEV)
+    ek, ev = torch.empty_like(case.dst_k), torch.empty_like(case.dst_v)
+    ews = torch.empty_like(ws)
+
+    def call(dk, dv, w):
+        pa.paged_kv_copy_blocks(case.src_k, case.src_v, dk, dv, case.src_to_dst, workspace=w)
+
+    g = capture(lambda: call(case.dst_k, case.dst_v, ws))
+    gen = torch.Generator(device="cpu").manual_seed(44)
+    for r in range(REPLAYS):
+        refill(case.src_k, gen)
+        refill(case.src_v, gen)
+        for t in (case.dst_k, case.dst_v, ek, ev):
+            t.fill_(-3.0)
+        g.replay()
+        torch.cuda.synchronize()
+        call(ek, ev, ews)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(case.dst_k), bits(ek)), f"replay {r}: K"
+        assert torch.equal(bits(case.dst_v), bits(ev)), f"replay {r}: V"
+    n_src, n_dst = case.src_k.shape[0], case.dst_k.shape[0]
+    sentinel = torch.full((1,), -3.0, dtype=case.dst_k.dtype).view(torch.int16).item()
+    want = copy_blocks_ref(host(bits(case.src_k)).reshape(n_src, -1),
+                           np.full((n_dst, case.dst_k[0].numel()), sentinel, dtype=np.int16),
+                           mapping)
+    assert np.array_equal(host(bits(case.dst_k)).reshape(n_dst, -1), want)
