@@ -25,10 +25,13 @@
  *     where they are declared: the block manager lives in host memory it
  *     allocates, the unfused baseline takes host length arrays and creates a
  *     matrix-library handle, and the copy accepts pinned host pools.)
- *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
- *     Calls only enqueue work: they return before the GPU finishes, never
- *     synchronise, and are safe to call from several host threads on
- *     different streams.  Calls that share a workspace must not overlap.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream);
+ *     it belongs to the current HIP device, like the arrays.  The library's
+ *     per-device state (CU count, kernel attributes, the matrix-library
+ *     handle) is keyed by the current device.  Calls only enqueue work:
+ *     they return before the GPU finishes, never synchronise, and are safe
+ *     to call from several host threads on different streams.  Calls that
+ *     share a workspace must not overlap.
  *   - Every call validates its host-side arguments first and returns a
  *     pa_status_t; nothing is launched unless the result is PA_OK.  Errors
  *     never abort or throw.  A launch failure reported by HIP is PA_ERR_LAUNCH.

@@ -121,9 +121,18 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream) -> ctypes.c_void_p:
+def _stream(stream, anchor: torch.Tensor) -> ctypes.c_void_p:
+    """Handle of `stream` (None: torch's current stream).  The library works on
+    the current HIP device, so the call's device tensors (represented by
+    `anchor`) and the stream must belong to it."""
+    dev = torch.cuda.current_device()
+    if anchor.device.index != dev:
+        raise ValueError(f"tensors are on {anchor.device} but the current device is cuda:{dev}; "
+                         f"call under torch.cuda.device({anchor.device.index})")
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(dev)
+    elif hasattr(stream, "device") and stream.device.index != dev:
+        raise ValueError(f"stream belongs to {stream.device}, the current device is cuda:{dev}")
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
@@ -187,7 +196,7 @@ def paged_attn_decode(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Ten
                                _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, bs,
                                nblk, mbps, int(max_context_len), float(scale), _DTYPE[dt],
                                int(partition_size), _ptr(workspace), workspace.numel(),
-                               _stream(stream))
+                               _stream(stream, query))
     _check(st, "paged_attn_decode")
     return out
 
@@ -223,7 +232,7 @@ def paged_attn_prefill(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Te
                                 _ptr(block_tables), _ptr(context_lens), _ptr(query_start_loc),
                                 B, T, int(max_query_len), int(max_context_len), Hq, Hkv, D, bs,
                                 nblk, block_tables.shape[1], float(scale), _DTYPE[dt],
-                                _stream(stream))
+                                _stream(stream, query))
     _check(st, "paged_attn_prefill")
     return out
 
@@ -287,7 +296,7 @@ def paged_attn_prefill_unfused(out: torch.Tensor, query: torch.Tensor, k_cache: 
         _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         ctypes.c_void_p(cl.data_ptr()), ctypes.c_void_p(qsl.data_ptr()), B, T, Hq, Hkv, D, bs,
         nblk, block_tables.shape[1], float(scale), _DTYPE[dt], _ptr(workspace),
-        workspace.numel(), _stream(stream))
+        workspace.numel(), _stream(stream, query))
     _check(st, "paged_attn_prefill_unfused")
     return out
 
@@ -300,7 +309,7 @@ def pa_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     _need(src, "src")
     _need(sink, "sink", torch.int32, 1)
     _check(lib.pa_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
-                              sink.numel(), _stream(stream)), "pa_stream_read")
+                              sink.numel(), _stream(stream, src)), "pa_stream_read")
 
 
 def paged_kv_append(k_cache: torch.Tensor, v_cache: Optional[torch.Tensor], key: torch.Tensor,
@@ -339,7 +348,7 @@ def paged_kv_append(k_cache: torch.Tensor, v_cache: Optional[torch.Tensor], key:
     st = lib.paged_kv_append(_ptr(k_cache), _ptr(v_cache), _ptr(key), _ptr(value),
                              _ptr(block_tables), _ptr(context_lens), _ptr(query_start_loc),
                              B, T, Hkv, D, bs, nblk, block_tables.shape[1], _DTYPE[dt],
-                             _stream(stream))
+                             _stream(stream, key))
     _check(st, "paged_kv_append")
 
 
@@ -399,7 +408,7 @@ def paged_kv_copy_blocks(src_k: torch.Tensor, src_v: Optional[torch.Tensor], dst
                                   _pool_ptr(dst_k, "dst_k"), _pool_ptr(dst_v, "dst_v"),
                                   _ptr(src_to_dst), src_to_dst.numel(), num_src, num_dst,
                                   block_bytes, _ptr(workspace), workspace.numel(),
-                                  _stream(stream))
+                                  _stream(stream, src_to_dst))
     _check(st, "paged_kv_copy_blocks")
 
 
