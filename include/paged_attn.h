@@ -59,7 +59,8 @@ typedef enum {
                                sizes are inconsistent (e.g. heads % kv_heads)   */
   PA_ERR_UNSUPPORTED = -4,  /* valid but not built: head_dim, block_size,
                                partition size, alignment                        */
-  PA_ERR_WORKSPACE = -5,    /* workspace NULL or smaller than the query says    */
+  PA_ERR_WORKSPACE = -5,    /* workspace NULL, smaller than the query says, or
+                               not 16-byte aligned                              */
   PA_ERR_LAUNCH = -6,       /* HIP reported an error while enqueueing           */
   PA_ERR_DEVICE = -7,       /* no usable HIP device is current                  */
   PA_ERR_NO_BLOCKS = -8,    /* block manager: no free physical block            */
@@ -111,8 +112,10 @@ const char *pa_status_string(pa_status_t status);
  *                PA_MAX_PARTITIONS partitions per sequence (else
  *                PA_ERR_UNSUPPORTED)
  *   workspace    device scratch of at least
- *                paged_attn_decode_workspace_size(...) bytes; contents on entry
- *                are ignored and are clobbered
+ *                paged_attn_decode_workspace_size(...) bytes, 16-byte aligned
+ *                (else PA_ERR_WORKSPACE: the kernels read its work list with
+ *                scalar loads and update its counter atomically); contents on
+ *                entry are ignored and are clobbered
  *
  * Supported: dtype f32/f16/bf16 (query, caches and out share it; arithmetic
  * is fp32), head_dim 64 or 128, block_size a power of two in [8, 256],
@@ -240,7 +243,8 @@ pa_status_t paged_attn_prefill_unfused(void *out, const void *query, const void 
  *   block_bytes   bytes per block, a positive multiple of 16; every pool
  *                 pointer 16-byte aligned
  *   workspace     device scratch of at least
- *                 paged_kv_copy_blocks_workspace_size(num_dst_blocks) bytes
+ *                 paged_kv_copy_blocks_workspace_size(num_dst_blocks) bytes,
+ *                 16-byte aligned (else PA_ERR_WORKSPACE)
  *
  * Source and destination pools must not overlap.  num_mappings may be 0
  * (nothing is launched) and must be below 2^31.

@@ -89,7 +89,7 @@ const char *pa_status_string(pa_status_t s) {
     case PA_ERR_DTYPE: return "PA_ERR_DTYPE: dtype unknown or not supported by this operation";
     case PA_ERR_SHAPE: return "PA_ERR_SHAPE: invalid or inconsistent sizes";
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: head_dim, block_size, partition or alignment not supported";
-    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing, too small or not 16-byte aligned";
     case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: HIP reported an error while enqueueing";
     case PA_ERR_DEVICE: return "PA_ERR_DEVICE: no usable HIP device";
     case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: no free physical block";
@@ -141,7 +141,7 @@ pa_status_t paged_attn_decode(void *out, const void *query, const void *k_cache,
     return PA_ERR_UNSUPPORTED;
   const pa::DecodeWorkspace ws =
       pa::decode_workspace_layout(num_seqs, num_heads, num_kv_heads, head_dim, nparts);
-  if (!workspace || workspace_bytes < ws.total) return PA_ERR_WORKSPACE;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < ws.total) return PA_ERR_WORKSPACE;
   if (!device_ok()) return PA_ERR_DEVICE;
   pa::DecodeLaunch a;
   a.out = out;
@@ -385,7 +385,8 @@ pa_status_t paged_kv_copy_blocks(const void *src_k, const void *src_v, void *dst
   if ((src_v == nullptr) != (dst_v == nullptr)) return PA_ERR_NULL;
   if (!aligned16(src_k) || !aligned16(dst_k) || (src_v && (!aligned16(src_v) || !aligned16(dst_v))))
     return PA_ERR_UNSUPPORTED;
-  if (!workspace || workspace_bytes < paged_kv_copy_blocks_workspace_size(num_dst_blocks))
+  if (!workspace || !aligned16(workspace) ||
+      workspace_bytes < paged_kv_copy_blocks_workspace_size(num_dst_blocks))
     return PA_ERR_WORKSPACE;
   if (!device_ok()) return PA_ERR_DEVICE;
   pa::CopyLaunch a;

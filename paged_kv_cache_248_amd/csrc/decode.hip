@@ -42,6 +42,7 @@
 //     physical block, so permuting the pool leaves results bit-identical.
 #include <atomic>
 
+#include "../../include/paged_attn.h"
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -838,6 +839,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(void *out, const floa
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Dynamic LDS the merge kernel is allowed once its attribute is raised: the
+// largest request, 16 heads x PA_MAX_PARTITIONS weights (the attribute is set
+// once per device, so it covers every later launch).
+constexpr size_t merge_lds_limit = (size_t)16 * PA_MAX_PARTITIONS * sizeof(float);
+static_assert(merge_lds_limit <= (160u << 10), "merge weights fit the 160 KiB LDS of a CU");
+
 template <class E, int D, int GT, bool MF>
 hipError_t launch_typed(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStream_t stream) {
   char *w = static_cast<char *>(a.workspace);
@@ -901,11 +908,27 @@ hipError_t launch_typed(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStr
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, stream, p);
   profile_end(stream);
   if (a.max_parts > 1) {
+    // The merge keeps GT x max_parts weights in LDS: up to 16 x 2048 x 4 =
+    // 128 KiB, past the 64 KiB a launch gets without the attribute.  The
+    // attribute belongs to the function on one device: bit d of this
+    // per-instantiation mask records that device d has it (devices past 63
+    // set it on every call).
+    const size_t merge_lds = (size_t)GT * a.max_parts * sizeof(float);
+    if (merge_lds > (64u << 10)) {
+      static std::atomic<uint64_t> attr_devices{0};
+      const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t{1} << dev : 0;
+      if (bit == 0 || (attr_devices.load(std::memory_order_relaxed) & bit) == 0) {
+        const hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&decode_merge_kernel<E, D, GT>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)merge_lds_limit);
+        if (e != hipSuccess) return e;
+        attr_devices.fetch_or(bit, std::memory_order_relaxed);
+      }
+    }
     hipLaunchKernelGGL((decode_merge_kernel<E, D, GT>),
-                       dim3(a.num_kv_heads * p.head_chunks, a.num_seqs), dim3(256),
-                       (size_t)GT * a.max_parts * sizeof(float), stream, a.out, p.part_o,
-                       p.part_ml, a.context_lens, a.num_heads, p.group, p.head_chunks,
-                       a.partition, a.max_parts, a.ctx_cap);
+                       dim3(a.num_kv_heads * p.head_chunks, a.num_seqs), dim3(256), merge_lds,
+                       stream, a.out, p.part_o, p.part_ml, a.context_lens, a.num_heads, p.group,
+                       p.head_chunks, a.partition, a.max_parts, a.ctx_cap);
   }
   return hipGetLastError();
 }
