@@ -136,6 +136,36 @@ pa_status_t paged_attn_decode(void *out, const void *query, const void *k_cache,
                               void *workspace, size_t workspace_bytes, void *stream);
 
 /* --------------------------------------------------------------------------
+ * Paged decode that allocates nothing.
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * operation, arguments, kernels and result as paged_attn_decode, bit for bit,
+ * but without a workspace argument.  The work list, counters and split-KV
+ * partials live in a static device array of PA_DECODE_NOALLOC_SCRATCH_BYTES
+ * bytes inside the library; each GPU the library runs on holds its own copy
+ * from the first call on it until the process ends.  A call whose
+ * paged_attn_decode_workspace_size(...) exceeds that size returns
+ * PA_ERR_WORKSPACE before launching anything (64 MiB holds, e.g., 128
+ * sequences x 32 heads x 16 partitions of head_dim 128).  The array keeps the
+ * last call's contents; every call re-initialises what it reads.  All calls
+ * on one GPU share the array: calls that may overlap in time on one GPU (two
+ * streams, two host threads) race and must be serialised by the caller.
+ * The call performs no hipMalloc/hipFree and calls no allocating library
+ * routine; the first call on a device looks up the array's device address.
+ * ------------------------------------------------------------------------ */
+#define PA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+pa_status_t paged_attn_decode_noalloc(void *out, const void *query, const void *k_cache,
+                                      const void *v_cache, const int32_t *block_tables,
+                                      const int32_t *context_lens, int32_t num_seqs,
+                                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t num_blocks,
+                                      int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      float scale, pa_dtype_t dtype, int32_t partition_size,
+                                      void *stream);
+
+/* --------------------------------------------------------------------------
  * Causal paged prefill / append.
  *
  * The new tokens of sequence b are rows query_start_loc[b] ..

@@ -17,7 +17,8 @@ import torch
 
 __all__ = [
     "PagedAttnError", "library_path", "load_library",
-    "paged_attn_decode", "paged_attn_decode_workspace_size",
+    "paged_attn_decode", "paged_attn_decode_workspace_size", "paged_attn_decode_noalloc",
+    "DECODE_NOALLOC_SCRATCH_BYTES",
     "paged_attn_prefill", "paged_attn_prefill_unfused", "paged_attn_prefill_unfused_workspace_size",
     "paged_kv_copy_blocks", "paged_kv_copy_blocks_workspace_size",
     "paged_kv_append", "BlockManager", "OutOfBlocksError",
@@ -27,6 +28,7 @@ __all__ = [
 _HERE = os.path.dirname(os.path.abspath(__file__))
 DEFAULT_PARTITION = 512       # PA_DEFAULT_PARTITION
 DEFAULT_PARTITION_GQA = 2048  # PA_DEFAULT_PARTITION_GQA
+DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20   # PA_DECODE_NOALLOC_SCRATCH_BYTES
 
 
 def default_partition(num_heads: int, num_kv_heads: int) -> int:
@@ -47,6 +49,9 @@ _SIGS = {
     "paged_attn_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32,
                                           _I32, _I32, _I32, _I32, ctypes.c_float, ctypes.c_int,
                                           _I32, _VP, _SZ, _VP]),
+    "paged_attn_decode_noalloc": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32,
+                                                  _I32, _I32, _I32, _I32, _I32, ctypes.c_float,
+                                                  ctypes.c_int, _I32, _VP]),
     "paged_attn_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32,
                                            _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                            ctypes.c_float, ctypes.c_int, _VP]),
@@ -156,19 +161,7 @@ def paged_attn_decode_workspace_size(num_seqs: int, num_heads: int, num_kv_heads
         num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size))
 
 
-def paged_attn_decode(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor,
-                      v_cache: torch.Tensor, block_tables: torch.Tensor,
-                      context_lens: torch.Tensor, scale: float,
-                      max_context_len: Optional[int] = None, partition_size: int = 0,
-                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """out[b,h] = softmax(scale * q[b,h] K_b^T) V_b over the paged cache.
-
-    query/out [B, Hq, D]; k_cache/v_cache [num_blocks, Hkv, block_size, D];
-    block_tables int32 [B, max_blocks]; context_lens int32 [B].
-    ``max_context_len`` (host int) bounds context_lens; None means
-    max_blocks * block_size.  partition_size: 0 = default, -1 = never split.
-    """
-    lib = load_library()
+def _decode_shapes(out, query, k_cache, v_cache, block_tables, context_lens):
     _need(query, "query", dims=3)
     dt = query.dtype
     if dt not in _DTYPE:
@@ -184,7 +177,46 @@ def paged_attn_decode(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Ten
     nblk, Hkv, bs, Dk = k_cache.shape
     if Dk != D or block_tables.shape[0] != B or context_lens.shape[0] != B:
         raise ValueError("inconsistent shapes")
-    mbps = block_tables.shape[1]
+    return B, Hq, Hkv, D, nblk, bs, block_tables.shape[1], dt
+
+
+def paged_attn_decode_noalloc(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor,
+                              v_cache: torch.Tensor, block_tables: torch.Tensor,
+                              context_lens: torch.Tensor, scale: float,
+                              max_context_len: Optional[int] = None, partition_size: int = 0,
+                              stream=None) -> torch.Tensor:
+    """paged_attn_decode without a workspace: the library keeps the work
+    list and split-KV partials in its own static device array
+    (DECODE_NOALLOC_SCRATCH_BYTES per GPU), so the call allocates nothing.
+    Calls that overlap in time on one GPU share that array and race."""
+    lib = load_library()
+    B, Hq, Hkv, D, nblk, bs, mbps, dt = _decode_shapes(out, query, k_cache, v_cache,
+                                                       block_tables, context_lens)
+    if max_context_len is None:
+        max_context_len = mbps * bs
+    st = lib.paged_attn_decode_noalloc(_ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D,
+                                       bs, nblk, mbps, int(max_context_len), float(scale),
+                                       _DTYPE[dt], int(partition_size), _stream(stream, query))
+    _check(st, "paged_attn_decode_noalloc")
+    return out
+
+
+def paged_attn_decode(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, block_tables: torch.Tensor,
+                      context_lens: torch.Tensor, scale: float,
+                      max_context_len: Optional[int] = None, partition_size: int = 0,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out[b,h] = softmax(scale * q[b,h] K_b^T) V_b over the paged cache.
+
+    query/out [B, Hq, D]; k_cache/v_cache [num_blocks, Hkv, block_size, D];
+    block_tables int32 [B, max_blocks]; context_lens int32 [B].
+    ``max_context_len`` (host int) bounds context_lens; None means
+    max_blocks * block_size.  partition_size: 0 = default, -1 = never split.
+    """
+    lib = load_library()
+    B, Hq, Hkv, D, nblk, bs, mbps, dt = _decode_shapes(out, query, k_cache, v_cache,
+                                                       block_tables, context_lens)
     if max_context_len is None:
         max_context_len = mbps * bs
     need = paged_attn_decode_workspace_size(B, Hq, Hkv, D, max_context_len, partition_size)

@@ -111,14 +111,16 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int
   return pa::decode_workspace_layout(num_seqs, num_heads, num_kv_heads, head_dim, nparts).total;
 }
 
-pa_status_t paged_attn_decode(void *out, const void *query, const void *k_cache,
-                              const void *v_cache, const int32_t *block_tables,
-                              const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
-                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                              int32_t num_blocks, int32_t max_blocks_per_seq,
-                              int32_t max_context_len, float scale, pa_dtype_t dtype,
-                              int32_t partition_size, void *workspace, size_t workspace_bytes,
-                              void *stream) {
+// Shared by paged_attn_decode (caller workspace) and paged_attn_decode_noalloc
+// (noalloc: the library's static scratch array, workspace arguments unused).
+static pa_status_t decode_call(void *out, const void *query, const void *k_cache,
+                               const void *v_cache, const int32_t *block_tables,
+                               const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq,
+                               int32_t max_context_len, float scale, pa_dtype_t dtype,
+                               int32_t partition_size, bool noalloc, void *workspace,
+                               size_t workspace_bytes, void *stream) {
   if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
       num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
@@ -141,8 +143,16 @@ pa_status_t paged_attn_decode(void *out, const void *query, const void *k_cache,
     return PA_ERR_UNSUPPORTED;
   const pa::DecodeWorkspace ws =
       pa::decode_workspace_layout(num_seqs, num_heads, num_kv_heads, head_dim, nparts);
-  if (!workspace || !aligned16(workspace) || workspace_bytes < ws.total) return PA_ERR_WORKSPACE;
+  if (noalloc) {
+    if (ws.total > PA_DECODE_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+  } else if (!workspace || !aligned16(workspace) || workspace_bytes < ws.total) {
+    return PA_ERR_WORKSPACE;
+  }
   if (!device_ok()) return PA_ERR_DEVICE;
+  if (noalloc) {
+    workspace = pa::decode_noalloc_scratch();
+    if (!workspace) return PA_ERR_DEVICE;
+  }
   pa::DecodeLaunch a;
   a.out = out;
   a.query = query;
@@ -164,6 +174,34 @@ pa_status_t paged_attn_decode(void *out, const void *query, const void *k_cache,
   a.dtype = (pa::DType)dtype;
   a.workspace = workspace;
   return launch_status(pa::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+pa_status_t paged_attn_decode(void *out, const void *query, const void *k_cache,
+                              const void *v_cache, const int32_t *block_tables,
+                              const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, int32_t max_blocks_per_seq,
+                              int32_t max_context_len, float scale, pa_dtype_t dtype,
+                              int32_t partition_size, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+  return decode_call(out, query, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                     num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, dtype, partition_size, false,
+                     workspace, workspace_bytes, stream);
+}
+
+pa_status_t paged_attn_decode_noalloc(void *out, const void *query, const void *k_cache,
+                                      const void *v_cache, const int32_t *block_tables,
+                                      const int32_t *context_lens, int32_t num_seqs,
+                                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t num_blocks,
+                                      int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      float scale, pa_dtype_t dtype, int32_t partition_size,
+                                      void *stream) {
+  return decode_call(out, query, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                     num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, dtype, partition_size, true,
+                     nullptr, 0, stream);
 }
 
 pa_status_t paged_attn_prefill(void *out, const void *query, const void *k_cache,

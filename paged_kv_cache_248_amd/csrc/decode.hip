@@ -979,6 +979,31 @@ DecodeWorkspace decode_workspace_layout(int64_t num_seqs, int64_t num_heads, int
   return w;
 }
 
+// ---- Scratch of the allocation-free entry point --------------------------
+// paged_attn_decode_noalloc keeps the work list, the counters and the
+// split-KV partials of a call here instead of in a caller workspace.  Every
+// GPU the library runs on holds its own copy of this array, at its own
+// address, from the first use until the process ends; every call on that GPU
+// uses the same copy, so calls that overlap on one GPU race.  The host-side
+// name is only a stand-in: kernels get the device address looked up below.
+static __device__ __align__(256) char scratch[PA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+void *decode_noalloc_scratch() {
+  static std::atomic<void *> per_device[64];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void *ptr = per_device[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  // Once per device, with that device current (two threads racing here
+  // store the same address).
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+    (void)hipGetLastError();     // leave no sticky error for the next call
+    return nullptr;
+  }
+  per_device[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+
 hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream) {
   const DecodeWorkspace ws = decode_workspace_layout(a.num_seqs, a.num_heads, a.num_kv_heads,
                                                      a.head_dim, a.max_parts);

@@ -35,6 +35,11 @@ DecodeWorkspace decode_workspace_layout(int64_t num_seqs, int64_t num_heads, int
 
 hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream);
 
+// Device address of this device's copy of the decode scratch array
+// (PA_DECODE_NOALLOC_SCRATCH_BYTES bytes, 256-byte aligned), looked up once
+// per device; nullptr if no device is current or the lookup fails.
+void *decode_noalloc_scratch();
+
 struct PrefillLaunch {
   void *out;
   const void *query;

@@ -339,3 +339,41 @@ def test_stream_read_validation(lib):
     if not gpu_available():
         assert lib.pa_stream_read(P, 32, P2, 8, None) == PA_ERR_DEVICE
 
+
+def _decode_noalloc(lib, **kw):
+    a = dict(out=P, query=P, k=P, v=P, bt=P, cl=P, B=2, Hq=8, Hkv=2, D=128, bs=16, nblk=64,
+             mbps=8, maxctx=100, scale=0.125, dtype=1, part=0, stream=None)
+    a.update(kw)
+    return lib.paged_attn_decode_noalloc(a["out"], a["query"], a["k"], a["v"], a["bt"], a["cl"],
+                                         a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["nblk"],
+                                         a["mbps"], a["maxctx"], a["scale"], a["dtype"],
+                                         a["part"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=7), PA_ERR_DTYPE),
+    (dict(Hq=6, Hkv=4), PA_ERR_SHAPE),
+    (dict(D=96), PA_ERR_UNSUPPORTED),
+    (dict(query=None), PA_ERR_NULL),
+    (dict(out=P + 2), PA_ERR_UNSUPPORTED),
+    # 128 seqs x 64 heads x 64 partitions x 128 floats of partials: past the
+    # library's scratch array, refused before any launch
+    (dict(B=128, Hq=64, Hkv=64, mbps=2048, maxctx=32768, part=512), PA_ERR_WORKSPACE),
+    (dict(B=0), PA_OK),
+])
+def test_decode_noalloc_validation(lib, kw, want):
+    assert _decode_noalloc(lib, **kw) == want
+
+
+def test_decode_noalloc_limit_matches_the_workspace_query(lib):
+    """The largest call the scratch array takes is the one whose workspace
+    query fits PA_DECODE_NOALLOC_SCRATCH_BYTES."""
+    limit = pa.DECODE_NOALLOC_SCRATCH_BYTES
+    assert "#define PA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in open(HEADER).read()
+    fits = lib.paged_attn_decode_workspace_size(128, 32, 8, 128, 32768, 2048)
+    assert 0 < fits <= limit
+    too_big = lib.paged_attn_decode_workspace_size(128, 64, 64, 128, 32768, 512)
+    assert too_big > limit
+    if not gpu_available():
+        # within the limit, a valid call reaches the device check
+        assert _decode_noalloc(lib, B=128, Hq=32, Hkv=8, mbps=2048, maxctx=32768) == PA_ERR_DEVICE
