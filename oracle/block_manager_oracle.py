@@ -12,17 +12,17 @@ Page cited (by title):
              growth, release) and §四.2 (prefix sharing by reference counts,
              copy-on-write when a request writes into a shared block).
 
-Steps, in the page's order:
-  * the pool starts with every block free; the free list is kept sorted, and
-    an allocation takes its lowest id and sets that block's count to 1; an
-    empty free list is an out-of-blocks error;
-  * releasing a block lowers its count if it is above 0; at 0 the block
-    returns to the free list (which is sorted again);
-  * registering a request of n prompt tokens allocates ceil(n / block_size)
-    blocks, in order, and records n tokens;
-  * appending one token to a request whose token count is a multiple of
-    block_size (its blocks are full) first allocates one more block; if that
-    fails the request is left unchanged and the append reports failure;
+What the page fixes (restated as rules, not as its listing):
+  * a physical block is free exactly when no request holds it: the manager
+    keeps one reference count per block, and the free blocks are those at 0;
+  * an allocation hands out the lowest-numbered free block and gives it a
+    count of 1; with no free block it is an out-of-blocks error;
+  * a release lowers the block's count by one (at 0 the block is free again);
+  * a request of n prompt tokens is registered with ceil(n / block_size)
+    newly allocated blocks, in logical order, and a token count of n;
+  * one more token goes into slot n mod block_size of the last block, so a
+    request whose count n is a multiple of block_size needs a new block
+    first; if none is free the request is left unchanged and the append fails;
   * finishing a request releases each of its blocks.
 Readings where the page is descriptive only (§四.2):
   * fork: a new request shares every block of an existing one (each count
@@ -45,53 +45,53 @@ class OutOfBlocks(Exception):
 class BlockManagerOracle:
     def __init__(self, num_blocks: int, block_size: int):
         self.block_size = block_size
-        self.ref = [0] * num_blocks
-        self.free = list(range(num_blocks))
+        self.ref = [0] * num_blocks            # holders of each physical block
         self.tables: dict[int, list[int]] = {}
         self.tokens: dict[int, int] = {}
 
+    @property
+    def free(self) -> list[int]:
+        """Free block ids, increasing: the blocks nobody holds."""
+        return [b for b, holders in enumerate(self.ref) if holders == 0]
+
     # -- physical blocks --------------------------------------------------
     def _allocate(self) -> int:
-        if not self.free:
+        if 0 not in self.ref:
             raise OutOfBlocks()
-        b = self.free.pop(0)
-        self.ref[b] = 1
-        return b
+        lowest = self.ref.index(0)             # lowest id with no holder
+        self.ref[lowest] = 1
+        return lowest
 
     def _release(self, b: int) -> None:
-        if self.ref[b] > 0:
-            self.ref[b] -= 1
-            if self.ref[b] == 0:
-                self.free.append(b)
-                self.free.sort()
+        assert self.ref[b] > 0, "released a block nobody holds"
+        self.ref[b] -= 1
 
     # -- requests ---------------------------------------------------------
     def register(self, rid: int, prompt_len: int) -> None:
         if rid in self.tables:
             raise KeyError(rid)
-        need = (prompt_len + self.block_size - 1) // self.block_size
-        got = []
+        blocks = []
         try:
-            for _ in range(need):
-                got.append(self._allocate())
+            while len(blocks) * self.block_size < prompt_len:
+                blocks.append(self._allocate())
         except OutOfBlocks:
-            for b in got:
+            for b in blocks:
                 self._release(b)
             raise
-        self.tables[rid] = got
+        self.tables[rid] = blocks
         self.tokens[rid] = prompt_len
 
     def append_token(self, rid: int):
         """Returns None, or the (old, new) pair of a copy-on-write."""
-        table, n = self.tables[rid], self.tokens[rid]
+        blocks, n = self.tables[rid], self.tokens[rid]
+        slot = n % self.block_size
         cow = None
-        if n % self.block_size == 0:
-            table.append(self._allocate())
-        elif self.ref[table[-1]] > 1:
-            new = self._allocate()
-            old = table[-1]
+        if slot == 0:                          # every held slot is filled
+            blocks.append(self._allocate())
+        elif self.ref[blocks[-1]] > 1:         # the slot is in a shared block
+            old, new = blocks[-1], self._allocate()
             self._release(old)
-            table[-1] = new
+            blocks[-1] = new
             cow = (old, new)
         self.tokens[rid] = n + 1
         return cow
@@ -99,9 +99,10 @@ class BlockManagerOracle:
     def fork(self, parent: int, child: int) -> None:
         if child in self.tables:
             raise KeyError(child)
-        for b in self.tables[parent]:
+        shared = list(self.tables[parent])
+        for b in shared:
             self.ref[b] += 1
-        self.tables[child] = list(self.tables[parent])
+        self.tables[child] = shared
         self.tokens[child] = self.tokens[parent]
 
     def finish(self, rid: int) -> None:
@@ -110,4 +111,4 @@ class BlockManagerOracle:
         del self.tokens[rid]
 
     def free_count(self) -> int:
-        return len(self.free)
+        return self.ref.count(0)

@@ -56,6 +56,7 @@ def check_invariants(bm, nblocks, bs):
     assert list(refs) == bm.ref
     assert bm.free == sorted(bm.free)
     assert set(bm.free) == {b for b in range(nblocks) if refs[b] == 0}
+    assert bm.free_count() == len(bm.free)
 
 
 @pytest.mark.parametrize("seed", range(30))
@@ -130,12 +131,14 @@ def test_finish_of_a_fork_keeps_the_shared_blocks():
 
 
 # planted mistakes: each must make one of the pins above fail
-class _NoSort(BlockManagerOracle):
-    def _release(self, b):
-        if self.ref[b] > 0:
-            self.ref[b] -= 1
-            if self.ref[b] == 0:
-                self.free.append(b)
+class _HighestFirst(BlockManagerOracle):
+    # hands out the highest free id instead of the lowest
+    def _allocate(self):
+        if 0 not in self.ref:
+            raise OutOfBlocks()
+        b = len(self.ref) - 1 - self.ref[::-1].index(0)
+        self.ref[b] = 1
+        return b
 
 
 class _LateGrowth(BlockManagerOracle):
@@ -148,7 +151,14 @@ class _LateGrowth(BlockManagerOracle):
         return None
 
 
-@pytest.mark.parametrize("mutant", [_NoSort, _LateGrowth])
+class _KeepsOnFinish(BlockManagerOracle):
+    # a finished request's blocks are never returned
+    def finish(self, rid):
+        self.tables.pop(rid)
+        del self.tokens[rid]
+
+
+@pytest.mark.parametrize("mutant", [_HighestFirst, _LateGrowth, _KeepsOnFinish])
 def test_page_run_catches_mutations(golden_dir, mutant):
     g = json.load(open(os.path.join(golden_dir, "append_block_manager_example.json")))
     bm, counts, grew_at, table_b = replay_page_example(g, mutant)

@@ -303,15 +303,17 @@ def test_copy_page_example(golden_dir):
 
 
 def _copy_brute(src, dst, m):
+    """One forward pass over the mapping records, per destination, the first
+    position naming it; then each recorded (destination, position) pair is
+    applied when the position is a source block."""
+    first = {}
+    for i, d in enumerate(np.asarray(m).tolist()):
+        if 0 <= d < dst.shape[0]:
+            first.setdefault(d, i)
     out = dst.copy()
-    for d in range(dst.shape[0]):
-        first = None
-        for i in range(len(m)):
-            if m[i] == d:
-                first = i
-                break
-        if first is not None and first < src.shape[0]:
-            out[d] = src[first]
+    for d, i in first.items():
+        if i < src.shape[0]:
+            out[d] = src[i]
     return out
 
 
