@@ -36,7 +36,16 @@ METRIC = "paged decode KV GB/s (% of 8 TB/s HBM peak); prefill TFLOP/s (% MFMA p
 
 # Sources of the decode kernel: the traffic figure is only reported while
 # these match the version the counters were collected on.
-DECODE_SOURCES = ["paged_kv_cache_248_amd/csrc/decode.hip", "paged_kv_cache_248_amd/csrc/pa_device.h"]
+# Sources of each kernel: a kernel's HBM traffic figure (profiles/hbm_traffic.md)
+# is only reported while these match the version the counters were taken on.
+_CSRC = "paged_kv_cache_248_amd/csrc/"
+SOURCES = {
+    "decode": [_CSRC + "decode.hip", _CSRC + "pa_device.h"],
+    "prefill": [_CSRC + "prefill.hip", _CSRC + "pa_device.h"],
+    "copy": [_CSRC + "copy_blocks.hip", _CSRC + "pa_device.h"],
+    "append": [_CSRC + "append.hip", _CSRC + "pa_device.h"],
+}
+DECODE_SOURCES = SOURCES["decode"]
 
 
 def log(msg: str) -> None:
@@ -94,23 +103,45 @@ def timed_steps(torch, fn, steps: int, warmup: int, timer=None, between=None):
 
 
 def bench_decode(pa, torch, wl, case, steps, warmup):
+    """Decode steps over two copies of the inputs (query, pools, tables,
+    lengths) in turn, so that no step finds the previous step's K/V in the
+    caches (the 256 MB Infinity Cache and the L2s): every timed step streams
+    its K/V from HBM.  A shorter run that repeats one copy is reported beside
+    it (`*_same_input`) to show what warm caches would add."""
     kv = case.kv
-    out = torch.empty_like(case.query)
     B, Hq, D = case.query.shape
     Hkv = kv.k_cache.shape[1]
     maxctx = kv.max_context_len
-    ws = torch.empty(pa.paged_attn_decode_workspace_size(B, Hq, Hkv, D, maxctx,
-                                                         case.partition_size),
-                     dtype=torch.uint8, device=case.query.device)
+    copies = [(case.query, kv.k_cache, kv.v_cache, kv.block_tables, kv.context_lens),
+              tuple(t.clone() for t in (case.query, kv.k_cache, kv.v_cache, kv.block_tables,
+                                          kv.context_lens))]
+    outs = [torch.empty_like(case.query) for _ in copies]
+    wss = [torch.empty(pa.paged_attn_decode_workspace_size(B, Hq, Hkv, D, maxctx,
+                                                           case.partition_size),
+                       dtype=torch.uint8, device=case.query.device) for _ in copies]
+    n = [0]
 
     def step():
-        pa.paged_attn_decode(out, case.query, kv.k_cache, kv.v_cache, kv.block_tables,
-                             kv.context_lens, case.scale, maxctx,
-                             partition_size=case.partition_size, workspace=ws)
+        i = n[0] & 1
+        n[0] += 1
+        q, kc, vc, bt, cl = copies[i]
+        pa.paged_attn_decode(outs[i], q, kc, vc, bt, cl, case.scale, maxctx,
+                             partition_size=case.partition_size, workspace=wss[i])
+
+    def step_same():
+        q, kc, vc, bt, cl = copies[0]
+        pa.paged_attn_decode(outs[0], q, kc, vc, bt, cl, case.scale, maxctx,
+                             partition_size=case.partition_size, workspace=wss[0])
 
     timer = KernelTimer(pa, torch, steps)
     ms = timed_steps(torch, step, steps, warmup, timer)
     kms = timer.mean_ms()
+    same_steps = max(10, steps // 2)
+    timer_same = KernelTimer(pa, torch, same_steps)
+    ms_same = timed_steps(torch, step_same, same_steps, max(10, warmup // 10), timer_same)
+    kms_same = timer_same.mean_ms()
+    assert torch.equal(outs[0], outs[1]), "the two input copies gave different outputs"
+    del copies
     ctx = kv.context_lens.cpu().numpy()
     nbytes = wl.decode_kv_bytes(ctx, Hq, Hkv, D, kv.block_size, wl.ELEM_BYTES[case.dtype])
     return {
@@ -118,6 +149,9 @@ def bench_decode(pa, torch, wl, case, steps, warmup):
         "GBps": nbytes / (ms * 1e-3) / 1e9, "kernel_GBps": nbytes / (kms * 1e-3) / 1e9,
         "tokens_per_s": B / (ms * 1e-3),
         "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "timing": "two input copies alternated: every step reads its K/V from HBM",
+        "ms_per_step_same_input": ms_same, "kernel_ms_same_input": kms_same,
+        "kernel_GBps_same_input": nbytes / (kms_same * 1e-3) / 1e9,
         "num_seqs": B, "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
         "block_size": kv.block_size, "dtype": case.dtype,
         "context_mean": float(ctx.mean()), "context_min": int(ctx.min()),
@@ -143,8 +177,14 @@ def bench_prefill(pa, torch, wl, case, steps, warmup):
     ql = np.diff(qsl)
     T, Hq, D = case.query.shape
     flops = wl.prefill_flops(ctx, ql, Hq, D)
+    Hkv = kv.k_cache.shape[1]
+    e = wl.ELEM_BYTES[case.dtype]
+    # compulsory HBM bytes: Q read and O written once, K and V of every key
+    # of every (sequence, kv head) read once
+    hbm_bytes = 2 * T * Hq * D * e + 2 * int(ctx.sum()) * Hkv * D * e
     return {
         "workload": case.name, "ms_per_step": ms, "kernel_ms": kms, "flops": flops,
+        "hbm_bytes": hbm_bytes,
         "TFLOPs": flops / (ms * 1e-3) / 1e12, "kernel_TFLOPs": flops / (kms * 1e-3) / 1e12,
         "frac_mfma_peak": flops / (kms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
         "tokens_per_s": T / (ms * 1e-3), "num_seqs": len(ctx), "new_tokens": int(T),
@@ -386,6 +426,37 @@ def bench_stream_copy(torch, steps, warmup, nbytes: int = 2 << 30):
             "ms": ms, "GBps": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
+def bench_stream_copy_lib(pa, torch, steps, warmup, nbytes: int = 2 << 30, shapes=(0, 32, 128)):
+    """The library's own read+write stream (pa_stream_copy: the non-temporal
+    16-byte loads and stores of the block copy and the append) over a 2 GiB
+    copy, for a few grid sizes; the fastest is the practical read+write
+    ceiling the copy and append kernels are set beside.  Shapes: one 16 KiB
+    chunk per work-group, and grid-stride loops over 32 or 128 work-groups
+    per CU."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(3)
+    dst = torch.empty_like(src)
+    best = None
+    sweep = {}
+    for wgs in shapes:                    # 0: one 16 KiB chunk per work-group
+        timer = KernelTimer(pa, torch, steps)
+        for _ in range(warmup):
+            pa.pa_stream_copy(src, dst, wgs)
+        torch.cuda.synchronize()
+        for _ in range(steps):
+            timer.arm()
+            pa.pa_stream_copy(src, dst, wgs)
+            timer.disarm()
+        torch.cuda.synchronize()
+        ms = float(np.median([s.elapsed_time(e) for s, e in timer.pairs[:timer.i]]))
+        gbps = 2 * nbytes / (ms * 1e-3) / 1e9
+        sweep[str(wgs)] = round(gbps, 1)
+        if best is None or gbps > best[1]:
+            best = (wgs, gbps, ms)
+    return {"workload": "stream_copy_lib", "bytes_read": nbytes, "bytes_written": nbytes,
+            "ms": best[2], "GBps": best[1], "wgs_per_cu": best[0], "sweep_GBps": sweep,
+            "frac_hbm_peak": best[1] / HBM_PEAK_GBS}
+
+
 def bench_stream_read(pa, torch, steps, warmup, nbytes: int = 4 << 30):
     """A plain device read of known size (the library's read-stream probe):
     the practical HBM ceiling for the read-dominated decode kernels."""
@@ -451,8 +522,24 @@ def cpu_baseline(torch, wl, case, budget_s: float, min_s: float = 10.0):
         "value": nbytes / spent / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
         "sample": f"{calls} single-sequence oracle calls over the {B} sequences of {case.name} "
                   f"(all {Hq} heads, {passes} pass(es)), {spent:.1f} s of fp64 numpy",
-        "seconds": spent,
+        "seconds": spent, **host_info(),
     }
+
+
+def host_info() -> dict:
+    """The host the CPU baseline ran on: logical CPUs, the CPUs this process
+    may use, and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"os_cpu_count": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": model}
 
 
 def cpu_prefill_sample(torch, wl, case, budget_s: float = 5.0):
@@ -505,6 +592,16 @@ def cpu_copy_sample(torch, wl, case):
                       f"{spent:.2f} s"}
 
 
+def roofline(bound: str, kernel: str, achieved: float, peak: float, unit: str, kernel_ms: float,
+             work: int, work_unit: str, traffic, **extra) -> dict:
+    """One roofline object: the kernel's algorithmic work per launch over its
+    event-timed duration, against the MI355X peak of its bound."""
+    return {"bound": bound, "kernel": kernel, "achieved": round(achieved, 2), "peak": peak,
+            "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
+            "kernel_ms": round(kernel_ms, 5), "work_per_launch": work, "work_unit": work_unit,
+            **extra}
+
+
 def hbm_traffic(kernel_files, launches_key: str):
     """Calibrated HBM bytes per launch from the committed PMC summary, or None
     when the kernel sources changed since the counters were taken."""
@@ -525,6 +622,37 @@ def hbm_traffic(kernel_files, launches_key: str):
     return entry.get("bytes_per_launch")
 
 
+def rooflines(extra: dict, head: dict) -> dict:
+    """One roofline object per workload: the decode kernels, the copy and the
+    append against HBM, the prefill kernel against the dense bf16 matrix
+    peak (its HBM traffic is reported beside it)."""
+    out = {"llama7b_decode_f16": roofline(
+        "hbm", "decode_kernel", head["kernel_GBps"], HBM_PEAK_GBS, "GB/s", head["kernel_ms"],
+        head["bytes"], "bytes", hbm_traffic(SOURCES["decode"], "decode_kernel/llama7b_decode_f16"))}
+    kernels = {"gqa_decode_bf16": "decode_mfma_kernel", "long_decode_f16": "decode_kernel"}
+    for name, kern in kernels.items():
+        r = extra.get(name)
+        if r:
+            out[name] = roofline("hbm", kern, r["kernel_GBps"], HBM_PEAK_GBS, "GB/s",
+                                 r["kernel_ms"], r["bytes"], "bytes",
+                                 hbm_traffic(SOURCES["decode"], f"{kern}/{name}"))
+    r = extra.get("prefill_bf16")
+    if r:
+        out["prefill_bf16"] = roofline(
+            "mfma", "prefill_kernel", r["kernel_TFLOPs"], MFMA_BF16_PEAK_TFS, "TFLOP/s",
+            r["kernel_ms"], r["flops"], "flop",
+            hbm_traffic(SOURCES["prefill"], "prefill_kernel/prefill_bf16"),
+            algorithmic_hbm_bytes=r.get("hbm_bytes"))
+    for name, kern, src in (("copy_bf16", "copy_kernel", "copy"),
+                            ("append_bf16", "append_kernel", "append")):
+        r = extra.get(name)
+        if r:
+            out[name] = roofline("hbm", kern, r["kernel_GBps"], HBM_PEAK_GBS, "GB/s",
+                                 r["kernel_ms"], r["bytes"], "bytes",
+                                 hbm_traffic(SOURCES[src], f"{kern}/{name}"))
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -537,7 +665,8 @@ def main() -> int:
     ap.add_argument("--only", default=None, choices=["llama7b_decode_f16", "gqa_decode_bf16",
                                                        "long_decode_f16", "prefill_bf16",
                                                        "copy_bf16", "append_bf16", "swap_bf16",
-                                                       "stream_copy", "stream_read", "prefill_unfused_bf16",
+                                                       "stream_copy", "stream_copy_lib", "stream_read",
+                                                       "prefill_unfused_bf16",
                                                        "tiny_decode_f32", "block_manager"],
                     help="run one workload, print its result object and exit (profiling)")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
@@ -571,6 +700,9 @@ def main() -> int:
         return 0
     if args.only == "tiny_decode_f32":
         print(json.dumps(bench_tiny_decode(pa, torch, wl, args.steps, args.warmup)), flush=True)
+        return 0
+    if args.only == "stream_copy_lib":
+        print(json.dumps(bench_stream_copy_lib(pa, torch, args.steps, args.warmup)), flush=True)
         return 0
     if args.only == "stream_read":
         print(json.dumps(bench_stream_read(pa, torch, args.steps, args.warmup)), flush=True)
@@ -669,6 +801,24 @@ def main() -> int:
         r = bench_stream_read(pa, torch, min(args.steps, 50), min(args.warmup, 20))
         log(f"  plain read stream: {r['GBps']:.0f} GB/s")
         extra["stream_read"] = r
+        r = bench_stream_copy_lib(pa, torch, min(args.steps, 30), min(args.warmup, 10))
+        log(f"  library copy stream: {r['GBps']:.0f} GB/s (read + write; shape {r['wgs_per_cu']}: "
+            f"0 = 16 KiB per work-group, else work-groups per CU)")
+        extra["stream_copy_lib"] = r
+        for name in ("copy_bf16", "append_bf16"):
+            extra[name]["frac_of_copy_stream"] = round(extra[name]["kernel_GBps"] / r["GBps"], 4)
+            # the same probe at the kernel's own size (launch and drain costs
+            # weigh more on a small transfer)
+            half = extra[name]["bytes"] // 2 // 16 * 16
+            rs = bench_stream_copy_lib(pa, torch, min(args.steps, 30), min(args.warmup, 10),
+                                       nbytes=half, shapes=(0,))
+            extra[name]["copy_stream_same_size_GBps"] = round(rs["GBps"], 1)
+            extra[name]["frac_of_copy_stream_same_size"] = round(
+                extra[name]["kernel_GBps"] / rs["GBps"], 4)
+        for name in ("llama7b_decode_f16", "gqa_decode_bf16", "long_decode_f16"):
+            if name in extra:
+                extra[name]["frac_of_read_stream"] = round(
+                    extra[name]["kernel_GBps"] / extra["stream_read"]["GBps"], 4)
         torch.cuda.empty_cache()
 
     cpu = None
@@ -699,13 +849,11 @@ def main() -> int:
             "partition_size": res["partition_size"], "accumulation": "f32",
             "parallelism": "single GPU",
         },
-        "roofline": {
-            "bound": "hbm", "kernel": "decode_kernel",
-            "achieved": round(res["kernel_GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(res["kernel_GBps"] / HBM_PEAK_GBS, 4),
-            "traffic": hbm_traffic(DECODE_SOURCES, "decode_kernel/llama7b_decode_f16"),
-            "kernel_ms": round(res["kernel_ms"], 5), "bytes_per_launch": res["bytes"],
-        },
+        "roofline": roofline("hbm", "decode_kernel", res["kernel_GBps"], HBM_PEAK_GBS, "GB/s",
+                             res["kernel_ms"], res["bytes"], "bytes",
+                             hbm_traffic(SOURCES["decode"], "decode_kernel/llama7b_decode_f16"),
+                             bytes_per_launch=res["bytes"]),
+        "rooflines": rooflines(extra, res),
         "cpu_baseline": cpu,
         "cpu_oracle_other": cpu_other or None,
         "tokens_per_s": round(res["tokens_per_s"], 1),

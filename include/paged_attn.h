@@ -433,6 +433,22 @@ pa_status_t pa_set_profile_events(void *start, void *stop);
 pa_status_t pa_stream_read(const void *src, int64_t bytes, uint32_t *sink, int32_t sink_words,
                            void *stream);
 
+/* --------------------------------------------------------------------------
+ * Copy-stream probe (measurement only).
+ *
+ * Copies the `bytes` bytes at `src` to `dst` (device, both 16-byte aligned,
+ * bytes a multiple of 16, else PA_ERR_UNSUPPORTED; overlapping ranges are
+ * PA_ERR_SHAPE) with the non-temporal 16-byte loads and stores the block
+ * copy and the KV append issue.  wgs_per_cu <= 0: one 16 KiB chunk per
+ * work-group (the fastest shape measured); > 0: a grid-stride loop over at
+ * most wgs_per_cu work-groups per CU.  Its achieved GB/s (bytes read plus
+ * bytes written) is the practical read+write ceiling those two kernels are
+ * set beside (the block copy of [P-swap] swap_blocks moves every byte once
+ * in each direction).  Recorded by pa_set_profile_events like a main kernel.
+ * ------------------------------------------------------------------------ */
+pa_status_t pa_stream_copy(const void *src, void *dst, int64_t bytes, int32_t wgs_per_cu,
+                           void *stream);
+
 #ifdef __cplusplus
 }
 #endif

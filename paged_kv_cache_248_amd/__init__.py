@@ -63,6 +63,7 @@ _SIGS = {
     "paged_kv_copy_blocks_workspace_size": (_SZ, [_I64]),
     "pa_host_device_pointer": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_void_p)]),
     "pa_stream_read": (ctypes.c_int, [_VP, _I64, _VP, _I32, _VP]),
+    "pa_stream_copy": (ctypes.c_int, [_VP, _VP, _I64, _I32, _VP]),
     "pa_bm_create": (ctypes.c_int, [_I32, _I32, ctypes.POINTER(ctypes.c_void_p)]),
     "pa_bm_destroy": (None, [_VP]),
     "pa_bm_register": (ctypes.c_int, [_VP, _I64, _I64]),
@@ -342,6 +343,19 @@ def pa_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     _need(sink, "sink", torch.int32, 1)
     _check(lib.pa_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
                               sink.numel(), _stream(stream, src)), "pa_stream_read")
+
+
+def pa_stream_copy(src: torch.Tensor, dst: torch.Tensor, wgs_per_cu: int = 0, stream=None) -> None:
+    """Copy-stream probe: dst[:] = src with non-temporal 16-byte accesses
+    (measurement of the practical read+write ceiling)."""
+    lib = load_library()
+    _need(src, "src")
+    _need(dst, "dst")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst sizes differ")
+    _check(lib.pa_stream_copy(_ptr(src), _ptr(dst), nbytes, int(wgs_per_cu), _stream(stream, src)),
+           "pa_stream_copy")
 
 
 def paged_kv_append(k_cache: torch.Tensor, v_cache: Optional[torch.Tensor], key: torch.Tensor,

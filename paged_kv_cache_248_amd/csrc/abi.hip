@@ -390,6 +390,20 @@ pa_status_t pa_stream_read(const void *src, int64_t bytes, uint32_t *sink, int32
       pa::launch_stream_read(src, bytes, sink, sink_words, static_cast<hipStream_t>(stream)));
 }
 
+pa_status_t pa_stream_copy(const void *src, void *dst, int64_t bytes, int32_t wgs_per_cu,
+                           void *stream) {
+  if (bytes < 0) return PA_ERR_SHAPE;
+  if (bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (bytes == 0) return PA_OK;
+  if (!src || !dst) return PA_ERR_NULL;
+  if (!aligned16(src) || !aligned16(dst)) return PA_ERR_UNSUPPORTED;
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  if (s0 < d0 + (uintptr_t)bytes && d0 < s0 + (uintptr_t)bytes) return PA_ERR_SHAPE;   // overlap
+  if (!device_ok()) return PA_ERR_DEVICE;
+  return launch_status(
+      pa::launch_stream_copy(src, dst, bytes, wgs_per_cu, static_cast<hipStream_t>(stream)));
+}
+
 pa_status_t pa_host_device_pointer(void *host_ptr, void **device_ptr) {
   if (!host_ptr || !device_ptr) return PA_ERR_NULL;
   *device_ptr = nullptr;
@@ -417,7 +431,8 @@ pa_status_t paged_kv_copy_blocks(const void *src_k, const void *src_v, void *dst
     return PA_ERR_SHAPE;
   if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
   const int64_t slices = (block_bytes + 16383) / 16384;
-  if (num_dst_blocks > 0 && slices > (int64_t)INT32_MAX / num_dst_blocks) return PA_ERR_SHAPE;
+  // one work-group per (pool, destination block, slice)
+  if (num_dst_blocks > 0 && slices > (int64_t)(INT32_MAX / 2) / num_dst_blocks) return PA_ERR_SHAPE;
   if (num_mappings == 0 || num_dst_blocks == 0 || num_src_blocks == 0) return PA_OK;
   if (!src_k || !dst_k || !src_to_dst) return PA_ERR_NULL;
   if ((src_v == nullptr) != (dst_v == nullptr)) return PA_ERR_NULL;

@@ -115,6 +115,12 @@ pa_gemm_status launch_prefill_unfused(const UnfusedLaunch &a, hipStream_t stream
 hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, int32_t sink_words,
                               hipStream_t stream);
 
+// Copies `bytes` (a multiple of 16) from src to dst once: one 16 KiB chunk
+// per work-group (wgs_per_cu <= 0), or a grid-stride loop over at most
+// wgs_per_cu work-groups per CU.
+hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes, int32_t wgs_per_cu,
+                              hipStream_t stream);
+
 // Compute units of the current device (cached per device).
 int device_cu_count();
 

@@ -28,8 +28,8 @@
 //     sharing a SIMD keep both busy;
 //   * K and V tiles go from the paged cache straight into LDS
 //     (global_load_lds_dwordx4, no registers, no LDS write instructions), four
-//     stages each, issued by the matrix group between its MFMAs (after the
-//     first quarter of QK^T); completion is
+//     stages each, issued by each group in its softmax phase (the matrix
+//     phases carry only MFMAs and their operand reads); completion is
 //     awaited with exact vmcnt counts before the barrier that publishes a
 //     tile, so loads of the next tiles stay in flight across phases;
 //   * per 64-key tile a wavefront computes S^T = K Q^T (2 x D/16 MFMA
@@ -344,13 +344,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
     float m = -__builtin_inff();
     float l = 0.f;
 
-    // Matrix phase: S^T = K_j Q^T, then O^T += V^T_{j-1} P^T_{j-1}.  The
-    // MFMAs run in units of four (QK: one 32-key half, 4 k-steps; PV: one
-    // 32-wide d sub-tile); the operand reads of unit u+1 are issued before
-    // the MFMAs of unit u.  `between(kt)` issues tile loads after QK half kt.
-    constexpr int QU = KS / 4 * 2;                // QK units
-    constexpr int U = QU + DT;                    // all units
-    auto matrix_phase = [&](uint32_t kb, uint32_t vb, bool do_pv, auto &&between) {
+    // Matrix phase: S^T = K_j Q^T, then O^T += V^T_{j-1} P^T_{j-1}.
+    auto matrix_phase = [&](uint32_t kb, uint32_t vb, bool do_pv) {
       // One unit = one MFMA; the operand reads of unit u + AHEAD are issued
       // before the MFMA of unit u (same-box A/B: 7 ahead, one MFMA per unit,
       // +0.9% over groups of four MFMAs read one group ahead; 5 ahead +0.7%;
@@ -398,14 +393,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
             }();
             asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(R[u % (AHEAD + 1)]) : "i"(later < 15 ? later : 15));
             consume(std::integral_constant<int, u>{});
-            if constexpr (u == KS / 2 - 1) {
-              __builtin_amdgcn_sched_barrier(0);
-              between(0);
-              __builtin_amdgcn_sched_barrier(0);
-            }
         });
       };
-      (void)U;
       if (do_pv) pipeline(std::integral_constant<int, QN + PN>{});
       else pipeline(std::integral_constant<int, QN>{});
     };
@@ -463,10 +452,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
     };
 
     // Prologue.  Group 0 loads K_0 .. K_{NS-2} and waits for K_0; group 1
-    // loads V_0 .. V_{NS-3}.  Each then holds the block ids of its next tile.
-    // `ids` holds the block ids of the tile this group loads in its next
-    // matrix phase; they are fetched in the phase before it.
-    Ids ids;
+    // loads V_0 .. V_{NS-3}.
     wait_vm<0>();                                 // query fragments in registers
     if constexpr (GRP == 0) {
 #pragma unroll
@@ -475,8 +461,6 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
         ids_tie(pre);
         load_tile(tt, pre, 0, IPW);
       }
-      ids = fetch_ids(NS - 1);
-      ids_tie(ids);
       wait_vm<IPW * (NS - 2)>();
     } else {
 #pragma unroll
@@ -489,45 +473,43 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
     phase_sync();
 
     // Step j = phases 2j and 2j+1.  In both, the matrix group reads K_j (K
-    // stage j % NS) and V_{j-1} (V stage (j-1) % NS).  Group 0 loads
-    // K_{j+NS-1} in phase 2j and, before the barrier that ends phase 2j+1,
-    // waits for K_{j+1}; group 1 loads V_{j+NS-2} in phase 2j+1 and waits for
-    // V_j before the barrier that ends it.  A stage is refilled only after
-    // the barrier that ends the last phase reading it.
+    // stage j % NS) and V_{j-1} (V stage (j-1) % NS).  Each group issues its
+    // tile loads in its softmax phase, so the matrix phases carry only MFMAs
+    // and their operand reads: group 0 loads K_{j+NS-1} in phase 2j+1 and
+    // waits for K_{j+1} before the barrier that ends it; group 1 loads
+    // V_{j+NS-2} in phase 2j and waits for V_j before the barrier that ends
+    // phase 2j+1.  A stage is refilled only after the barrier that ends the
+    // last phase reading it.  The block ids of a load are fetched with scalar
+    // loads at the start of the softmax phase and awaited after the softmax
+    // (no LDS read is in flight there: scalar and LDS loads share a counter).
     for (int j = 0; j <= ntiles; ++j) {
       const uint32_t kb = lds0 + (j % NS) * TILE;
       const uint32_t vb = lds0 + (NS + (j + NS - 1) % NS) * TILE;
       const bool qk = j < wave_tiles;
       const bool pv = j >= 1 && j - 1 < wave_tiles;
       const int lt = GRP == 0 ? j + NS - 1 : j + NS - 2;     // tile loaded this step
-      // All of this step's tile loads go out after the first quarter of the
-      // QK^T MFMAs (four for head_dim 128).  Same-box A/B runs: issuing them
-      // all at one point beat splitting them over the two QK halves by 2.2%;
-      // of the points tried (phase start, after 2, 4, 6, 8 or 12 of the 16
-      // QK MFMAs) after 4 was fastest, 0.4% ahead of 2, 6 and 8.
-      auto between = [&](int kt) {
-        if (kt == 0) load_tile(lt, ids, 0, IPW);
-      };
       // The wavefront in its matrix phase runs at raised issue priority, so
       // that its operand reads and MFMAs win the SIMD's arbitration against
-      // the softmax wavefront beside it (measured +0.3%, same box A/B).
+      // the softmax wavefront beside it.
       if constexpr (GRP == 0) {
-        ids_tie(ids);                                     // phase 2j
-        __builtin_amdgcn_s_setprio(1);
-        matrix_phase(kb, vb, pv, between);
+        __builtin_amdgcn_s_setprio(1);                    // phase 2j
+        matrix_phase(kb, vb, pv);
         __builtin_amdgcn_s_setprio(0);
         phase_sync();
-        ids = fetch_ids(lt + 1);                          // phase 2j+1
+        Ids ids = fetch_ids(lt);                          // phase 2j+1
         if (qk) softmax(j);
+        ids_tie(ids);
+        load_tile(lt, ids, 0, IPW);
         wait_vm<kWaitSteady>();
         phase_sync();
       } else {
-        ids = fetch_ids(lt);                              // phase 2j
+        Ids ids = fetch_ids(lt);                          // phase 2j
         if (pv) softmax(j - 1);
+        ids_tie(ids);
+        load_tile(lt, ids, 0, IPW);
         phase_sync();
-        ids_tie(ids);                                     // phase 2j+1
-        __builtin_amdgcn_s_setprio(1);
-        matrix_phase(kb, vb, pv, between);
+        __builtin_amdgcn_s_setprio(1);                    // phase 2j+1
+        matrix_phase(kb, vb, pv);
         __builtin_amdgcn_s_setprio(0);
         wait_vm<kWaitSteady>();
         phase_sync();

@@ -377,3 +377,14 @@ def test_decode_noalloc_limit_matches_the_workspace_query(lib):
     if not gpu_available():
         # within the limit, a valid call reaches the device check
         assert _decode_noalloc(lib, B=128, Hq=32, Hkv=8, mbps=2048, maxctx=32768) == PA_ERR_DEVICE
+
+
+def test_stream_copy_validation(lib):
+    assert lib.pa_stream_copy(P, P2 + 0x100000, -16, 0, None) == PA_ERR_SHAPE
+    assert lib.pa_stream_copy(P, P2 + 0x100000, 24, 0, None) == PA_ERR_UNSUPPORTED    # not a multiple of 16
+    assert lib.pa_stream_copy(P + 8, P2 + 0x100000, 32, 0, None) == PA_ERR_UNSUPPORTED  # misaligned
+    assert lib.pa_stream_copy(None, P2, 32, 0, None) == PA_ERR_NULL
+    assert lib.pa_stream_copy(P, P + 16, 64, 0, None) == PA_ERR_SHAPE                 # overlapping
+    assert lib.pa_stream_copy(P, P2, 0, 0, None) == PA_OK
+    if not gpu_available():
+        assert lib.pa_stream_copy(P, P2 + 0x100000, 32, 0, None) == PA_ERR_DEVICE

@@ -21,3 +21,18 @@ def test_stream_read_reads_every_word_once(words, sink_words):
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert got == np.bitwise_xor.reduce(host.view(np.uint32))
+
+
+@pytest.mark.parametrize("nbytes,wgs", [(16, 0), (16 * 1023, 1), (16 * 12345, 64), (16 * 12345, 0),
+                                        ((64 << 20) + 16 * 777, 0), ((64 << 20) + 16 * 3, 128)])
+def test_stream_copy_copies_every_byte_once(nbytes, wgs):
+    """The copy probe reproduces the source bit for bit and writes nothing
+    past the destination range (guard words on both sides)."""
+    g = torch.Generator(device="cpu").manual_seed(nbytes + wgs)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g).cuda()
+    buf = torch.full((nbytes + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+    dst = buf[32:32 + nbytes]
+    pa.pa_stream_copy(src, dst, wgs)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    assert (buf[:32] == 0xA5).all() and (buf[32 + nbytes:] == 0xA5).all()
