@@ -67,6 +67,8 @@ typedef enum {
   PA_ERR_REQUEST = -9       /* block manager: unknown or duplicate request id   */
 } pa_status_t;
 
+/* Element types.  Entry points take the dtype as an int32_t holding one of
+ * these values; any other integer gives PA_ERR_DTYPE. */
 typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } pa_dtype_t;
 
 /* Library default KV partition length, in tokens, for split-KV decode:
@@ -79,8 +81,10 @@ typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } pa_dtype_
  * (ceil(min(max_context_len, max_blocks_per_seq*block_size) / partition)). */
 #define PA_MAX_PARTITIONS 2048
 
-/* Human-readable name of a status code (static string, never NULL). */
-const char *pa_status_string(pa_status_t status);
+/* Human-readable name of a status code (static string, never NULL).  Any
+ * integer is accepted: values that are not a pa_status_t give
+ * "PA_ERR_UNKNOWN". */
+const char *pa_status_string(int32_t status);
 
 /* --------------------------------------------------------------------------
  * Paged decode.
@@ -132,7 +136,7 @@ pa_status_t paged_attn_decode(void *out, const void *query, const void *k_cache,
                               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                               int32_t block_size, int32_t num_blocks,
                               int32_t max_blocks_per_seq, int32_t max_context_len,
-                              float scale, pa_dtype_t dtype, int32_t partition_size,
+                              float scale, int32_t dtype, int32_t partition_size,
                               void *workspace, size_t workspace_bytes, void *stream);
 
 /* --------------------------------------------------------------------------
@@ -162,7 +166,7 @@ pa_status_t paged_attn_decode_noalloc(void *out, const void *query, const void *
                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                       int32_t block_size, int32_t num_blocks,
                                       int32_t max_blocks_per_seq, int32_t max_context_len,
-                                      float scale, pa_dtype_t dtype, int32_t partition_size,
+                                      float scale, int32_t dtype, int32_t partition_size,
                                       void *stream);
 
 /* --------------------------------------------------------------------------
@@ -200,7 +204,7 @@ pa_status_t paged_attn_prefill(void *out, const void *query, const void *k_cache
                                int32_t max_query_len, int32_t max_context_len,
                                int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                int32_t block_size, int32_t num_blocks,
-                               int32_t max_blocks_per_seq, float scale, pa_dtype_t dtype,
+                               int32_t max_blocks_per_seq, float scale, int32_t dtype,
                                void *stream);
 
 /* --------------------------------------------------------------------------
@@ -243,7 +247,7 @@ pa_status_t paged_attn_prefill(void *out, const void *query, const void *k_cache
  * ------------------------------------------------------------------------ */
 size_t paged_attn_prefill_unfused_workspace_size(int32_t max_query_len, int32_t max_context_len,
                                                  int32_t num_heads, int32_t num_kv_heads,
-                                                 int32_t head_dim, pa_dtype_t dtype);
+                                                 int32_t head_dim, int32_t dtype);
 pa_status_t paged_attn_prefill_unfused(void *out, const void *query, const void *k_cache,
                                        const void *v_cache, const int32_t *block_tables,
                                        const int32_t *context_lens_host,
@@ -251,7 +255,7 @@ pa_status_t paged_attn_prefill_unfused(void *out, const void *query, const void 
                                        int32_t total_query_tokens, int32_t num_heads,
                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                        int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
-                                       pa_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                                       int32_t dtype, void *workspace, size_t workspace_bytes,
                                        void *stream);
 
 /* --------------------------------------------------------------------------
@@ -332,7 +336,7 @@ pa_status_t paged_kv_append(void *k_cache, void *v_cache, const void *key, const
                             const int32_t *query_start_loc, int32_t num_seqs,
                             int32_t total_tokens, int32_t num_kv_heads, int32_t head_dim,
                             int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
-                            pa_dtype_t dtype, void *stream);
+                            int32_t dtype, void *stream);
 
 /* --------------------------------------------------------------------------
  * Host block manager ([P-wall] §三, the allocator simulator; §四.2, prefix

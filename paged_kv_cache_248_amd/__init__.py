@@ -43,7 +43,7 @@ _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
 
 _SIGS = {
-    "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
     "pa_set_profile_events": (ctypes.c_int, [_VP, _VP]),
     "paged_attn_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "paged_attn_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32,
@@ -93,7 +93,9 @@ class PagedAttnError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, "libpagedattn.so")
+    """The in-tree library, or the file PA_LIBRARY names (the host-sanitized
+    build, for CPU runs of the host-side tests)."""
+    return os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpagedattn.so")
 
 
 def load_library():

@@ -82,7 +82,9 @@ pa_status_t pa_set_profile_events(void *start, void *stop) {
   return PA_OK;
 }
 
-const char *pa_status_string(pa_status_t s) {
+const char *pa_status_string(int32_t s) {
+  // an int, not the enum: callers may pass any integer, and a C++ enum
+  // object may not hold values outside its enumerators' range
   switch (s) {
     case PA_OK: return "PA_OK";
     case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
@@ -118,7 +120,7 @@ static pa_status_t decode_call(void *out, const void *query, const void *k_cache
                                const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                int32_t num_blocks, int32_t max_blocks_per_seq,
-                               int32_t max_context_len, float scale, pa_dtype_t dtype,
+                               int32_t max_context_len, float scale, int32_t dtype,
                                int32_t partition_size, bool noalloc, void *workspace,
                                size_t workspace_bytes, void *stream) {
   if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
@@ -181,7 +183,7 @@ pa_status_t paged_attn_decode(void *out, const void *query, const void *k_cache,
                               const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                               int32_t num_blocks, int32_t max_blocks_per_seq,
-                              int32_t max_context_len, float scale, pa_dtype_t dtype,
+                              int32_t max_context_len, float scale, int32_t dtype,
                               int32_t partition_size, void *workspace, size_t workspace_bytes,
                               void *stream) {
   return decode_call(out, query, k_cache, v_cache, block_tables, context_lens, num_seqs,
@@ -196,7 +198,7 @@ pa_status_t paged_attn_decode_noalloc(void *out, const void *query, const void *
                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                       int32_t block_size, int32_t num_blocks,
                                       int32_t max_blocks_per_seq, int32_t max_context_len,
-                                      float scale, pa_dtype_t dtype, int32_t partition_size,
+                                      float scale, int32_t dtype, int32_t partition_size,
                                       void *stream) {
   return decode_call(out, query, k_cache, v_cache, block_tables, context_lens, num_seqs,
                      num_heads, num_kv_heads, head_dim, block_size, num_blocks,
@@ -211,7 +213,7 @@ pa_status_t paged_attn_prefill(void *out, const void *query, const void *k_cache
                                int32_t max_query_len, int32_t max_context_len, int32_t num_heads,
                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
-                               pa_dtype_t dtype, void *stream) {
+                               int32_t dtype, void *stream) {
   if (dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
   if (!(scale > 0.0f) || !std::isfinite(scale)) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || total_query_tokens < 0 || max_query_len < 0 || max_context_len < 0 ||
@@ -256,7 +258,7 @@ pa_status_t paged_attn_prefill(void *out, const void *query, const void *k_cache
 
 size_t paged_attn_prefill_unfused_workspace_size(int32_t max_query_len, int32_t max_context_len,
                                                  int32_t num_heads, int32_t num_kv_heads,
-                                                 int32_t head_dim, pa_dtype_t dtype) {
+                                                 int32_t head_dim, int32_t dtype) {
   if ((dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) || max_query_len < 0 ||
       max_context_len < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0)
     return 0;
@@ -272,7 +274,7 @@ pa_status_t paged_attn_prefill_unfused(void *out, const void *query, const void 
                                        int32_t total_query_tokens, int32_t num_heads,
                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                        int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
-                                       pa_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                                       int32_t dtype, void *workspace, size_t workspace_bytes,
                                        void *stream) {
   if (dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
   if (!(scale > 0.0f) || !std::isfinite(scale)) return PA_ERR_UNSUPPORTED;
@@ -341,7 +343,7 @@ pa_status_t paged_kv_append(void *k_cache, void *v_cache, const void *key, const
                             const int32_t *query_start_loc, int32_t num_seqs,
                             int32_t total_tokens, int32_t num_kv_heads, int32_t head_dim,
                             int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
-                            pa_dtype_t dtype, void *stream) {
+                            int32_t dtype, void *stream) {
   if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
   const int32_t elem = dtype == PA_DTYPE_F32 ? 4 : 2;
   if (num_seqs < 0 || total_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 ||
