@@ -14,8 +14,8 @@
 //   * GQA: the query heads of one group share a single K/V read, addressed by
 //     index — the MQA/GQA remarks of the swap-mechanism page;
 //   * long contexts are cut into partitions processed in parallel, each
-//     leaving (M, L, O~) partials that a second kernel merges with the same
-//     rescaling (block-level parallelism, "vLLM中FlashAttention与KVCache优化解析",
+//     leaving (M, L, O~) partials that are merged with the same rescaling
+//     (block-level parallelism, "vLLM中FlashAttention与KVCache优化解析",
 //     FlashAttention advantages table).
 //
 // Design for CDNA4 (HBM-bound path, ~1-4 flop per byte):
@@ -26,10 +26,12 @@
 //     compact list built on device (full partitions first, the shorter last
 //     partitions at the end), so the kernel drains evenly whatever the mix of
 //     context lengths;
-//   * a sequence that spans several partitions leaves (M, L, O~) partials that
-//     a short merge kernel combines; the weights of a (sequence, head) are
-//     computed once in LDS and every partial is then read with independent
-//     loads, so the merge costs a few memory latencies, not one per partial;
+//   * a sequence that spans several partitions leaves (M, L, O~) partials;
+//     the work-group that stores the last partition of a (sequence, kv head,
+//     head chunk) — counted with an atomic arrival counter, the partials
+//     written and read through the device-coherent path — merges them in the
+//     same kernel, so the merge costs no extra launch and overlaps the other
+//     work-groups' partitions;
 //   * a token row (D * elem bytes) is split into 16-byte pieces, one per lane:
 //     each load instruction moves 1 KiB fully coalesced; the lanes of one
 //     token reduce their partial dot products with DPP row exchanges;
@@ -78,6 +80,7 @@ struct DecodeParams {
   int32_t *next_item;         // dynamic work counter (zeroed by the plan kernel)
   float *part_o;              // [B, Hq, max_parts, D] unnormalised O
   float *part_ml;             // [B, Hq, max_parts, 2] (M in log2 units, L)
+  int32_t *arrive;            // [B, Hkv, head_chunks] partitions finished (zeroed by the plan kernel)
   int32_t num_heads, num_kv_heads, group, head_chunks;
   int32_t bs_log2, max_blocks_per_seq, num_blocks;
   int32_t partition, max_parts, ctx_cap;
@@ -180,11 +183,94 @@ __device__ __forceinline__ void store_elem(void *out, size_t idx, float v) {
 
 constexpr int kWaves = 4;
 
+// Device-coherent store and load of split-KV partials (agent-scope relaxed
+// atomics: the write-through / coherent-read cache policy), so that a
+// work-group on any XCD reads what another one wrote without a device-wide
+// cache write-back or invalidate.
+__device__ __forceinline__ void coherent_store(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Split-KV merge of one (sequence, kv head, head chunk), run inside the
+// decode kernel by the work-group that stores its last partition's partials:
+// M = max_p M_p, L = sum_p L_p 2^(M_p - M), O = sum_p O~_p 2^(M_p - M) / L —
+// the OnlineSoftmax rescaling applied across partitions.  Wavefront w forms
+// M and 1/L of heads w, w + 4, ... by wave-level reductions (kept in
+// s_mm / s_il); then each thread takes (head, dim) pairs and reads their
+// partials a few at a time, recomputing each weight from (M_p, L).
+template <class E, int D, int GT>
+__device__ __forceinline__ void merge_partials(const DecodeParams &p, int b, int h0, int nh,
+                                               int nparts, float *s_mm, float *s_il) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int j = wave; j < nh; j += kWaves) {
+    const float *ml = p.part_ml + ((size_t)b * p.num_heads + h0 + j) * p.max_parts * 2;
+    float mx = -__builtin_inff();
+    for (int q = lane; q < nparts; q += 64) mx = fmaxf(mx, coherent_load(&ml[2 * q]));
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
+    float ls = 0.f;
+    for (int q = lane; q < nparts; q += 64)
+      ls = fmaf(fast_exp2(coherent_load(&ml[2 * q]) - mx), coherent_load(&ml[2 * q + 1]), ls);
+    for (int off = 32; off > 0; off >>= 1) ls += shfl_xor(ls, off);
+    if (lane == 0) {
+      s_mm[j] = mx;
+      s_il[j] = 1.0f / ls;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < nh * D; idx += kWaves * 64) {
+    const int j = idx / D, d = idx % D;
+    const size_t row = (size_t)b * p.num_heads + h0 + j;
+    const float *po = p.part_o + row * p.max_parts * D + d;
+    const float *ml = p.part_ml + row * p.max_parts * 2;
+    const float M = s_mm[j];
+    // kBatch partials per round, all loads in flight together; past the
+    // last partition the index is clamped (a cached re-read) and the weight
+    // is 0
+    constexpr int kBatch = 4;
+    float acc = 0.f;
+    for (int q0 = 0; q0 < nparts; q0 += kBatch) {
+      float v[kBatch], mq[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int q = min(q0 + u, nparts - 1);
+        v[u] = coherent_load(&po[(size_t)q * D]);
+        mq[u] = coherent_load(&ml[2 * q]);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        acc = fmaf(q0 + u < nparts ? fast_exp2(mq[u] - M) : 0.f, v[u], acc);
+    }
+    store_elem<E>(p.out, row * D + d, acc * s_il[j]);
+  }
+}
+
+// After a work-group has stored the partials of a partition of a
+// multi-partition sequence (coherent stores): every wavefront waits until
+// its stores are complete, then one thread counts the partition; the
+// work-group that counts the last partition of a (sequence, kv head, head
+// chunk) merges, reading the partials coherently after it saw the count.
+// Called by every thread of the work-group (it synchronises).
+template <class E, int D, int GT>
+__device__ __forceinline__ void finish_partition(const DecodeParams &p, int b, int g, int hc, int h0,
+                                                 int nh, int nparts, int *s_flag, float *s_mm,
+                                                 float *s_il) {
+  wait_vm<0>();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *s_flag = atomicAdd(p.arrive + ((size_t)b * p.num_kv_heads + g) * p.head_chunks + hc, 1) ==
+              nparts - 1;
+  __syncthreads();
+  if (*s_flag) merge_partials<E, D, GT>(p, b, h0, nh, nparts, s_mm, s_il);
+}
+
 template <class E, int D, int GT>
 __global__ __launch_bounds__(256, GT == 4 ? 4 : 2) void decode_kernel(DecodeParams p) {
   using G = Geom<E, D, GT>;
   constexpr int NL = G::kNL, TPL = G::kTPL, LPT = G::kLPT, EPL = G::kEPL, TILE = G::kTile;
-  __shared__ int s_item;
+  __shared__ int s_item, s_flag;
   __shared__ float s_m[kWaves][GT], s_l[kWaves][GT];
   __shared__ __attribute__((aligned(16))) float s_o[kWaves][GT][D];
 
@@ -394,14 +480,18 @@ __global__ __launch_bounds__(256, GT == 4 ? 4 : 2) void decode_kernel(DecodePara
       if (nparts <= 1) {
         store_elem<E>(p.out, row * D + d, O / L);
       } else {
+        // partials go through the device-coherent path (another work-group,
+        // possibly on another XCD, merges them)
         const size_t slot = row * p.max_parts + part;
-        p.part_o[slot * D + d] = O;
+        coherent_store(&p.part_o[slot * D + d], O);
         if (d == 0) {
-          p.part_ml[slot * 2] = M;
-          p.part_ml[slot * 2 + 1] = L;
+          coherent_store(&p.part_ml[slot * 2], M);
+          coherent_store(&p.part_ml[slot * 2 + 1], L);
         }
       }
     }
+    if (nparts > 1)
+      finish_partition<E, D, GT>(p, b, g, hc, h0, nh, nparts, &s_flag, s_m[0], s_l[0]);
     __syncthreads();   // LDS and s_item are reused by the next item
   }
 }
@@ -472,7 +562,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeParams p) {
   static_assert(GT >= 4 && GT <= 16, "one 16-column MFMA block of heads");
   static_assert(kWaves * GT * D * 4 <= kWaves * NST * TILEB, "partials fit the V stages");
   __shared__ __attribute__((aligned(1024))) char s_v[kWaves * NST * TILEB];
-  __shared__ int s_item;
+  __shared__ int s_item, s_flag;
   __shared__ float s_m[kWaves][GT], s_l[kWaves][GT];
   float(*s_o)[GT][D] = reinterpret_cast<float(*)[GT][D]>(s_v);   // after the key loop
 
@@ -699,37 +789,43 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeParams p) {
       if (nparts <= 1) {
         store_elem<E>(p.out, row * D + d, O / L);
       } else {
+        // partials go through the device-coherent path (another work-group,
+        // possibly on another XCD, merges them)
         const size_t slot = row * p.max_parts + part;
-        p.part_o[slot * D + d] = O;
+        coherent_store(&p.part_o[slot * D + d], O);
         if (d == 0) {
-          p.part_ml[slot * 2] = M;
-          p.part_ml[slot * 2 + 1] = L;
+          coherent_store(&p.part_ml[slot * 2], M);
+          coherent_store(&p.part_ml[slot * 2 + 1], L);
         }
       }
     }
+    if (nparts > 1)
+      finish_partition<E, D, GT>(p, b, g, hc, h0, nh, nparts, &s_flag, s_m[0], s_l[0]);
     __syncthreads();   // LDS and s_item are reused by the next item
   }
 }
 
 // Builds the compact list of (sequence, partition) work items — full-length
 // partitions first, then the shorter last partitions — and clears the
-// dynamic work counter.  With long partitions (lpt set: 1024 tokens or more,
-// a few items per work-group) the last partitions go longest first (in 32
-// length classes), so that work-groups taking items in list order end on
-// short ones (GQA workload, 2048-token partitions: +5.5% kernel bandwidth);
-// with short partitions (many items per work-group) they stay in sequence
-// order (the headline MHA workload, 512-token partitions, measured 0.7%
-// slower in length order).
+// dynamic work counter and the merge arrival counters.  With long
+// partitions (lpt set: 1024 tokens or more, a few items per work-group) the
+// last partitions go longest first (in 32 length classes), so that
+// work-groups taking items in list order end on short ones (GQA workload,
+// 2048-token partitions: +5.5% kernel bandwidth); with short partitions
+// (many items per work-group) they stay in sequence order (the headline MHA
+// workload, 512-token partitions, measured 0.7% slower in length order).
 __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t *context_lens, int num_seqs,
                                                            int partition, int ctx_cap, int lpt,
                                                            int32_t *work, int32_t *work_count,
-                                                           int32_t *next_item) {
+                                                           int32_t *next_item, int32_t *arrive,
+                                                           int n_arrive) {
   constexpr int kClasses = 32;
   __shared__ int s_full[1024], s_tail[1024];
   __shared__ int s_total_full;
   __shared__ int s_class[kClasses];      // last partitions per length class, then their next slot
   const int tid = threadIdx.x;
   auto tail_class = [&](int tail) { return (int)((long long)tail * kClasses / partition); };
+  for (int i = tid; i < n_arrive; i += 1024) arrive[i] = 0;   // merge arrival counters
   if (tid < kClasses) s_class[tid] = 0;
   __syncthreads();
   // pass 1: number of full partitions over all sequences, and the last
@@ -803,71 +899,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t *contex
 }
 
 
-// Merges the partition partials of one (sequence, kv head, head chunk):
-// M = max_p M_p, L = sum_p L_p 2^(M_p - M), O = sum_p O~_p 2^(M_p - M) / L —
-// the OnlineSoftmax rescaling applied across partitions.  Wavefront w forms
-// the weights 2^(M_p - M) / L of heads w, w+4, ... in LDS with wave-level
-// reductions; then every (head, dim) sum reads its partials 32 at a time, so
-// a sequence of many partitions costs a few memory round trips.
-template <class E, int D, int GT>
-__global__ __launch_bounds__(256) void decode_merge_kernel(void *out, const float *part_o,
-                                                          const float *part_ml,
-                                                          const int32_t *context_lens,
-                                                          int num_heads, int group,
-                                                          int head_chunks, int partition,
-                                                          int max_parts, int ctx_cap) {
-  extern __shared__ float s_w[];                  // [GT][max_parts]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = blockIdx.y;
-  const int hc = blockIdx.x % head_chunks;
-  const int g = blockIdx.x / head_chunks;
-  const int ctx = min(max(context_lens[b], 0), ctx_cap);
-  const int nparts = (ctx + partition - 1) / partition;
-  if (nparts <= 1) return;
-  const int h0 = g * group + hc * GT;
-  const int nh = min(GT, group - hc * GT);
-  for (int j = wave; j < nh; j += 4) {
-    const float *ml = part_ml + ((size_t)b * num_heads + h0 + j) * max_parts * 2;
-    float mx = -__builtin_inff();
-    for (int q = lane; q < nparts; q += 64) mx = fmaxf(mx, ml[2 * q]);
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
-    float ls = 0.f;
-    for (int q = lane; q < nparts; q += 64) {
-      const float c = fast_exp2(ml[2 * q] - mx);
-      s_w[j * max_parts + q] = c;
-      ls = fmaf(c, ml[2 * q + 1], ls);
-    }
-    for (int off = 32; off > 0; off >>= 1) ls += shfl_xor(ls, off);
-    const float inv = 1.0f / ls;
-    for (int q = lane; q < nparts; q += 64) s_w[j * max_parts + q] *= inv;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < nh * D; idx += 256) {
-    const int j = idx / D, d = idx % D;
-    const size_t row = (size_t)b * num_heads + h0 + j;
-    const float *po = part_o + row * max_parts * D + d;
-    const float *w = s_w + j * max_parts;
-    // 32 partials per round, all loads in flight together; past the last
-    // partition the index is clamped (a cached re-read) and the weight is 0
-    float acc = 0.f;
-    for (int q0 = 0; q0 < nparts; q0 += 32) {
-      float v[32];
-#pragma unroll
-      for (int u = 0; u < 32; ++u) v[u] = po[(size_t)min(q0 + u, nparts - 1) * D];
-#pragma unroll
-      for (int u = 0; u < 32; ++u) acc = fmaf(q0 + u < nparts ? w[q0 + u] : 0.f, v[u], acc);
-    }
-    store_elem<E>(out, row * D + d, acc);
-  }
-}
-
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
-// Dynamic LDS the merge kernel is allowed once its attribute is raised: the
-// largest request, 16 heads x PA_MAX_PARTITIONS weights (the attribute is set
-// once per device, so it covers every later launch).
-constexpr size_t merge_lds_limit = (size_t)16 * PA_MAX_PARTITIONS * sizeof(float);
-static_assert(merge_lds_limit <= (160u << 10), "merge weights fit the 160 KiB LDS of a CU");
 
 template <class E, int D, int GT, bool MF>
 hipError_t launch_typed(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStream_t stream) {
@@ -884,6 +916,7 @@ hipError_t launch_typed(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStr
   p.next_item = reinterpret_cast<int32_t *>(w + ws.count_off + 4);
   p.part_o = reinterpret_cast<float *>(w + ws.part_o_off);
   p.part_ml = reinterpret_cast<float *>(w + ws.part_ml_off);
+  p.arrive = reinterpret_cast<int32_t *>(w + ws.arrive_off);
   p.num_heads = a.num_heads;
   p.num_kv_heads = a.num_kv_heads;
   p.group = a.num_heads / a.num_kv_heads;
@@ -905,7 +938,8 @@ hipError_t launch_typed(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStr
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, a.context_lens,
                        a.num_seqs, a.partition, a.ctx_cap, a.partition >= 1024 ? 1 : 0,
                        reinterpret_cast<int32_t *>(w + ws.work_off),
-                       reinterpret_cast<int32_t *>(w + ws.count_off), p.next_item);
+                       reinterpret_cast<int32_t *>(w + ws.count_off), p.next_item, p.arrive,
+                       a.num_seqs * a.num_kv_heads * p.head_chunks);
 
   // Resident work-groups per CU; items are fetched dynamically, so a grid
   // larger than what fits only queues (it cannot unbalance the work).
@@ -931,29 +965,6 @@ hipError_t launch_typed(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStr
   profile_begin(stream);
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, stream, p);
   profile_end(stream);
-  if (a.max_parts > 1) {
-    // The merge keeps GT x max_parts weights in LDS: up to 16 x 2048 x 4 =
-    // 128 KiB, past the 64 KiB a launch gets without the attribute.  The
-    // attribute belongs to the function on one device: bit d of this
-    // per-instantiation mask records that device d has it (devices past 63
-    // set it on every call).
-    const size_t merge_lds = (size_t)GT * a.max_parts * sizeof(float);
-    if (merge_lds > (64u << 10)) {
-      static std::atomic<uint64_t> attr_devices{0};
-      const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t{1} << dev : 0;
-      if (bit == 0 || (attr_devices.load(std::memory_order_relaxed) & bit) == 0) {
-        const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&decode_merge_kernel<E, D, GT>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)merge_lds_limit);
-        if (e != hipSuccess) return e;
-        attr_devices.fetch_or(bit, std::memory_order_relaxed);
-      }
-    }
-    hipLaunchKernelGGL((decode_merge_kernel<E, D, GT>),
-                       dim3(a.num_kv_heads * p.head_chunks, a.num_seqs), dim3(256), merge_lds,
-                       stream, a.out, p.part_o, p.part_ml, a.context_lens, a.num_heads, p.group,
-                       p.head_chunks, a.partition, a.max_parts, a.ctx_cap);
-  }
   return hipGetLastError();
 }
 
@@ -986,12 +997,16 @@ hipError_t launch_dim(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStrea
 
 DecodeWorkspace decode_workspace_layout(int64_t num_seqs, int64_t num_heads, int64_t num_kv_heads,
                                         int64_t head_dim, int64_t max_parts) {
-  // counts (work_count, next_item) | work list | partials
+  // counts (work_count, next_item) | work list | merge arrival counters
+  // (one per sequence and query head: at least one per (sequence, kv head,
+  // head chunk)) | partials
   (void)num_kv_heads;
   DecodeWorkspace w;
   w.count_off = 0;
   w.work_off = 256;
   size_t off = align_up(w.work_off + (size_t)num_seqs * max_parts * 2 * sizeof(int32_t), 256);
+  w.arrive_off = off;
+  off = align_up(off + (size_t)num_seqs * num_heads * sizeof(int32_t), 256);
   w.part_o_off = off;
   w.part_ml_off = off;
   if (max_parts > 1) {

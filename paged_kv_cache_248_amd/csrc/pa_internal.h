@@ -28,7 +28,7 @@ struct DecodeLaunch {
 
 // Workspace layout of the decode path, shared by size query and launcher.
 struct DecodeWorkspace {
-  size_t count_off, work_off, part_o_off, part_ml_off, total;
+  size_t count_off, work_off, arrive_off, part_o_off, part_ml_off, total;
 };
 DecodeWorkspace decode_workspace_layout(int64_t num_seqs, int64_t num_heads, int64_t num_kv_heads,
                                         int64_t head_dim, int64_t max_parts);

@@ -152,9 +152,10 @@ def test_prefill_planted_keys_long_context(dtype, bs):
 @pytest.mark.parametrize("dtype,ctx", [("bf16", [70001, 999]), ("f16", [131072])])
 def test_decode_merge_over_1024_partitions_large_group(dtype, ctx):
     """16 query heads per kv head, 64-token partitions, contexts over 65536
-    keys: 1094 and 2048 (the most allowed) partitions, so the merge keeps
-    16 x partitions x 4 bytes of weights in LDS (70 KiB and 128 KiB, past
-    the 64 KiB a launch gets by default).  Every row against the oracle."""
+    keys: 1094 and 2048 (the most allowed) partitions merged by one
+    work-group per (sequence, kv head) — the in-kernel merge's largest case
+    (16 x 2048 weights, recomputed per partial).  Every row against the
+    oracle."""
     ctx = np.array(ctx)
     case = wl.make_decode(ctx, 32, 2, 128, 16, dtype, seed=4600 + len(ctx), device=DEV,
                           poison=True)
