@@ -814,36 +814,46 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeParams p) {
 // 2048-token partitions: +5.5% kernel bandwidth); with short partitions
 // (many items per work-group) they stay in sequence order (the headline MHA
 // workload, 512-token partitions, measured 0.7% slower in length order).
-__global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t *context_lens, int num_seqs,
-                                                           int partition, int ctx_cap, int lpt,
-                                                           int32_t *work, int32_t *work_count,
-                                                           int32_t *next_item, int32_t *arrive,
-                                                           int n_arrive) {
-  constexpr int kClasses = 32;
-  __shared__ int s_full[1024], s_tail[1024];
+// Inclusive prefix sum and total over one wavefront (shuffles, no barrier).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off, 64);
+    if (lane >= off) v += u;
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(256) void decode_plan_kernel(const int32_t *context_lens, int num_seqs,
+                                                          int partition, int ctx_cap, int lpt,
+                                                          int32_t *work, int32_t *work_count,
+                                                          int32_t *next_item, int32_t *arrive,
+                                                          int n_arrive) {
+  constexpr int kClasses = 32, kT = 256;
+  __shared__ int s_wave[kT / 64][2];     // per-wavefront totals (full, last partitions)
   __shared__ int s_total_full;
   __shared__ int s_class[kClasses];      // last partitions per length class, then their next slot
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   auto tail_class = [&](int tail) { return (int)((long long)tail * kClasses / partition); };
-  for (int i = tid; i < n_arrive; i += 1024) arrive[i] = 0;   // merge arrival counters
+  for (int i = tid; i < n_arrive; i += kT) arrive[i] = 0;   // merge arrival counters
   if (tid < kClasses) s_class[tid] = 0;
   __syncthreads();
   // pass 1: number of full partitions over all sequences, and the last
   // partitions per length class
   int full_sum = 0;
-  for (int b = tid; b < num_seqs; b += 1024) {
+  for (int b = tid; b < num_seqs; b += kT) {
     const int ctx = min(max(context_lens[b], 0), ctx_cap);
     full_sum += ctx / partition;
     if (lpt && ctx % partition) atomicAdd(&s_class[tail_class(ctx % partition)], 1);
   }
-  s_full[tid] = full_sum;
+  full_sum = wave_incl_scan(full_sum);
+  if (lane == 63) s_wave[wave][0] = full_sum;
   __syncthreads();
-  for (int off = 512; off > 0; off >>= 1) {
-    if (tid < off) s_full[tid] += s_full[tid + off];
-    __syncthreads();
-  }
   if (tid == 0) {
-    s_total_full = s_full[0];
+    int tf = 0;
+    for (int w = 0; w < kT / 64; ++w) tf += s_wave[w][0];
+    s_total_full = tf;
     // first slot of each class, longest class first
     int acc = 0;
     for (int k = kClasses - 1; k >= 0; --k) {
@@ -854,43 +864,43 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t *contex
   }
   __syncthreads();
   const int total_full = s_total_full;
-  __syncthreads();
-  // pass 2: place items, chunk by chunk of 1024 sequences
+  // pass 2: place items, 256 sequences at a time
   int base_full = 0, base_tail = 0;
-  for (int c0 = 0; c0 < num_seqs; c0 += 1024) {
+  for (int c0 = 0; c0 < num_seqs; c0 += kT) {
     const int b = c0 + tid;
-    int nf = 0, nt = 0;
+    int nf = 0, nt = 0, tail = 0;
     if (b < num_seqs) {
       const int ctx = min(max(context_lens[b], 0), ctx_cap);
       nf = ctx / partition;
-      nt = (ctx % partition) != 0;
+      tail = ctx % partition;
+      nt = tail != 0;
     }
-    s_full[tid] = nf;
-    s_tail[tid] = nt;
+    const int sf = wave_incl_scan(nf), st = wave_incl_scan(nt);
+    __syncthreads();                      // s_wave of the previous chunk is read
+    if (lane == 63) {
+      s_wave[wave][0] = sf;
+      s_wave[wave][1] = st;
+    }
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int a = tid >= off ? s_full[tid - off] : 0;
-      const int c = tid >= off ? s_tail[tid - off] : 0;
-      __syncthreads();
-      s_full[tid] += a;
-      s_tail[tid] += c;
-      __syncthreads();
+    int pf = 0, pt = 0, tf = 0, tt = 0;
+    for (int w = 0; w < kT / 64; ++w) {
+      if (w < wave) pf += s_wave[w][0], pt += s_wave[w][1];
+      tf += s_wave[w][0];
+      tt += s_wave[w][1];
     }
-    const int f0 = base_full + s_full[tid] - nf;
+    const int f0 = base_full + pf + sf - nf;
     for (int k = 0; k < nf; ++k) {
       work[2 * (f0 + k)] = b;
       work[2 * (f0 + k) + 1] = k;
     }
     if (nt) {
-      const int ctx = min(max(context_lens[b], 0), ctx_cap);
-      const int t0 = total_full + (lpt ? atomicAdd(&s_class[tail_class(ctx % partition)], 1)
-                                       : base_tail + s_tail[tid] - 1);
+      const int t0 = total_full + (lpt ? atomicAdd(&s_class[tail_class(tail)], 1)
+                                       : base_tail + pt + st - 1);
       work[2 * t0] = b;
       work[2 * t0 + 1] = nf;
     }
-    base_full += s_full[1023];
-    base_tail += s_tail[1023];
-    __syncthreads();
+    base_full += tf;
+    base_tail += tt;
   }
   if (tid == 0) {
     *work_count = total_full + base_tail;
@@ -935,7 +945,7 @@ hipError_t launch_typed(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStr
   p.direct = a.max_parts == 1;
 
   if (!p.direct)
-    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, a.context_lens,
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(256), 0, stream, a.context_lens,
                        a.num_seqs, a.partition, a.ctx_cap, a.partition >= 1024 ? 1 : 0,
                        reinterpret_cast<int32_t *>(w + ws.work_off),
                        reinterpret_cast<int32_t *>(w + ws.count_off), p.next_item, p.arrive,
