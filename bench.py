@@ -236,7 +236,11 @@ def bench_prefill_unfused(pa, torch, wl, case, steps, warmup):
 def bench_tiny_decode(pa, torch, wl, steps, warmup):
     """The tiny fp32 decode (4 sequences, contexts up to 200 tokens): a
     launch-bound call, reported in microseconds per call, issued eagerly and
-    as the replay of a captured HIP graph (its launches recorded once)."""
+    as the replay of a captured HIP graph (its launches recorded once).
+    Beside each GPU-timeline rate: the host time to issue one call (the loop
+    without the final synchronisation) and, for the eager calls, the kernel's
+    own duration from the library's events, which show what bounds each
+    rate."""
     case = wl.tiny_decode_f32(device="cuda:0")
     kv = case.kv
     out = torch.empty_like(case.query)
@@ -252,30 +256,34 @@ def bench_tiny_decode(pa, torch, wl, steps, warmup):
 
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(steps):
-        call()
-    stop.record()
-    torch.cuda.synchronize()
-    eager_us = start.elapsed_time(stop) * 1e3 / steps
+
+    def rate(fn):
+        """(GPU-timeline us per call, host us to issue one call)"""
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        start.record()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        t1 = time.perf_counter()
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) * 1e3 / steps, (t1 - t0) * 1e6 / steps
+
+    eager_us, eager_host_us = rate(call)
+    timer = KernelTimer(pa, torch, steps)
+    timed_steps(torch, call, steps, 10, timer)
+    kernel_us = timer.mean_ms() * 1e3
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         call()
-    for _ in range(warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(steps):
-        g.replay()
-    stop.record()
-    torch.cuda.synchronize()
-    graph_us = start.elapsed_time(stop) * 1e3 / steps
+    graph_us, graph_host_us = rate(g.replay)
     ctx = kv.context_lens.cpu().numpy()
     return {"workload": "tiny_decode_f32", "eager_us_per_call": eager_us,
-            "graph_us_per_call": graph_us, "num_seqs": B, "num_heads": Hq, "head_dim": D,
+            "eager_host_us_per_call": eager_host_us, "kernel_us": kernel_us,
+            "graph_us_per_call": graph_us, "graph_host_us_per_replay": graph_host_us,
+            "num_seqs": B, "num_heads": Hq, "head_dim": D,
             "context_lens": ctx.tolist(), "steps": steps, "warmup": warmup}
 
 
@@ -739,7 +747,7 @@ def main() -> int:
     extra = {}
     cpu_other = {}
     if not args.quick:
-        r = bench_tiny_decode(pa, torch, wl, args.steps, min(args.warmup, 50))
+        r = bench_tiny_decode(pa, torch, wl, args.steps, args.warmup)
         log(f"  tiny_decode_f32: {r['eager_us_per_call']:.1f} us/call eager, "
             f"{r['graph_us_per_call']:.1f} us/call as a graph replay")
         extra["tiny_decode_f32"] = r
