@@ -487,6 +487,39 @@ def bench_stream_read(pa, torch, steps, warmup, nbytes: int = 4 << 30):
             "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_mfma_stream(pa, torch, steps, warmup, iters: int = 20000, shapes=(1, 2)):
+    """Back-to-back bf16 MFMA 32x32x16 on random operands over the whole GPU
+    (the library's matrix-core stream probe), at 1 and 2 work-groups of four
+    wavefronts per CU: the matrix cores' practical rate under the power limit
+    for random data, the ceiling the prefill is set beside."""
+    g = torch.Generator(device="cuda:0").manual_seed(2489)
+    ops = torch.randn(1 << 22, device="cuda:0", generator=g).to(torch.bfloat16)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sweep = {}
+    best = None
+    for w in shapes:
+        sink = torch.zeros(cus * w, dtype=torch.float32, device="cuda:0")
+        timer = KernelTimer(pa, torch, steps)
+        for _ in range(warmup):
+            pa.pa_mfma_stream(ops, sink, w, iters)
+        torch.cuda.synchronize()
+        for _ in range(steps):
+            timer.arm()
+            pa.pa_mfma_stream(ops, sink, w, iters)
+            timer.disarm()
+        torch.cuda.synchronize()
+        ms = float(np.median([s.elapsed_time(e) for s, e in timer.pairs[:timer.i]]))
+        flops = cus * w * 4 * iters * 32 * 2 * 32 * 32 * 16
+        tf = flops / (ms * 1e-3) / 1e12
+        sweep[str(w)] = round(tf, 1)
+        if best is None or tf > best[1]:
+            best = (w, tf, ms, flops)
+    w, tf, ms, flops = best
+    return {"workload": "mfma_stream_bf16", "wgs_per_cu": w, "waves_per_simd": w,
+            "flops": flops, "ms": ms, "TFLOPs": tf, "frac_mfma_peak": tf / MFMA_BF16_PEAK_TFS,
+            "sweep_TFLOPs": sweep}
+
+
 def cpu_baseline(torch, wl, case, budget_s: float, min_s: float = 10.0):
     """The fp64 oracle on the host cores, sequence by sequence, until the time
     budget is spent (whole passes are repeated until at least ``min_s``);
@@ -674,7 +707,7 @@ def main() -> int:
                                                        "long_decode_f16", "prefill_bf16",
                                                        "copy_bf16", "append_bf16", "swap_bf16",
                                                        "stream_copy", "stream_copy_lib", "stream_read",
-                                                       "prefill_unfused_bf16",
+                                                       "mfma_stream", "prefill_unfused_bf16",
                                                        "tiny_decode_f32", "block_manager"],
                     help="run one workload, print its result object and exit (profiling)")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
@@ -714,6 +747,10 @@ def main() -> int:
         return 0
     if args.only == "stream_read":
         print(json.dumps(bench_stream_read(pa, torch, args.steps, args.warmup)), flush=True)
+        return 0
+    if args.only == "mfma_stream":
+        print(json.dumps(bench_mfma_stream(pa, torch, min(args.steps, 20), min(args.warmup, 20))),
+              flush=True)
         return 0
     if args.only == "prefill_unfused_bf16":
         log("generating prefill_bf16 ...")
@@ -827,6 +864,13 @@ def main() -> int:
             if name in extra:
                 extra[name]["frac_of_read_stream"] = round(
                     extra[name]["kernel_GBps"] / extra["stream_read"]["GBps"], 4)
+        r = bench_mfma_stream(pa, torch, min(args.steps, 20), min(args.warmup, 20))
+        log(f"  matrix-core stream: {r['TFLOPs']:.0f} TFLOP/s bf16 "
+            f"({r['wgs_per_cu']} work-group(s) of 4 waves per CU)")
+        extra["mfma_stream"] = r
+        if "prefill_bf16" in extra:
+            extra["prefill_bf16"]["frac_of_mfma_stream"] = round(
+                extra["prefill_bf16"]["kernel_TFLOPs"] / r["TFLOPs"], 4)
         torch.cuda.empty_cache()
 
     cpu = None

@@ -453,6 +453,28 @@ pa_status_t pa_stream_read(const void *src, int64_t bytes, uint32_t *sink, int32
 pa_status_t pa_stream_copy(const void *src, void *dst, int64_t bytes, int32_t wgs_per_cu,
                            void *stream);
 
+/* --------------------------------------------------------------------------
+ * Matrix-core stream probe (measurement only).
+ *
+ * Runs min(CUs x wgs_per_cu, sink_words) work-groups of four wavefronts
+ * (wgs_per_cu in [1, 8]); every wavefront performs `iters` (> 0) rounds of
+ * 32 back-to-back v_mfma_f32_32x32x16 (dtype PA_DTYPE_F16 or PA_DTYPE_BF16)
+ * on eight A and eight B operand fragments per lane that it reads once from
+ * `operands` (device, 16-byte aligned, operand_bytes >= 4096 and a multiple
+ * of 16; fragments are taken modulo the buffer, which should hold random
+ * data of the dtype), into four independent fp32 accumulators.  Work-group
+ * i writes the sum of its accumulators to sink[i] (device fp32).  Each
+ * work-group does 4 x iters x 32 x 32768 flops.  Its achieved TFLOP/s is the
+ * matrix cores' practical rate under the power limit for such data, with no
+ * memory or softmax work beside it: the ceiling the prefill (a dense
+ * contraction, [P-opt] 核心思想) is set beside.  Errors: PA_ERR_DTYPE,
+ * PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (size or alignment), PA_ERR_NULL,
+ * PA_ERR_DEVICE.  Recorded by pa_set_profile_events like a main kernel.
+ * ------------------------------------------------------------------------ */
+pa_status_t pa_mfma_stream(const void *operands, int64_t operand_bytes, float *sink,
+                           int32_t sink_words, int32_t wgs_per_cu, int32_t iters, int32_t dtype,
+                           void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,6 +64,7 @@ _SIGS = {
     "pa_host_device_pointer": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_void_p)]),
     "pa_stream_read": (ctypes.c_int, [_VP, _I64, _VP, _I32, _VP]),
     "pa_stream_copy": (ctypes.c_int, [_VP, _VP, _I64, _I32, _VP]),
+    "pa_mfma_stream": (ctypes.c_int, [_VP, _I64, _VP, _I32, _I32, _I32, _I32, _VP]),
     "pa_bm_create": (ctypes.c_int, [_I32, _I32, ctypes.POINTER(ctypes.c_void_p)]),
     "pa_bm_destroy": (None, [_VP]),
     "pa_bm_register": (ctypes.c_int, [_VP, _I64, _I64]),
@@ -358,6 +359,23 @@ def pa_stream_copy(src: torch.Tensor, dst: torch.Tensor, wgs_per_cu: int = 0, st
         raise ValueError("src and dst sizes differ")
     _check(lib.pa_stream_copy(_ptr(src), _ptr(dst), nbytes, int(wgs_per_cu), _stream(stream, src)),
            "pa_stream_copy")
+
+
+def pa_mfma_stream(operands: torch.Tensor, sink: torch.Tensor, wgs_per_cu: int, iters: int,
+                   stream=None) -> None:
+    """Matrix-core stream probe: min(CUs x wgs_per_cu, sink.numel()) work-groups
+    of four wavefronts, each wavefront `iters` rounds of 32 MFMA 32x32x16 on
+    operands (fp16 or bf16, random data) read once; work-group i writes the
+    sum of its accumulators to sink[i] (fp32)."""
+    lib = load_library()
+    _need(operands, "operands")
+    _need(sink, "sink", torch.float32)
+    if operands.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("operands must be float16 or bfloat16")
+    _check(lib.pa_mfma_stream(_ptr(operands), operands.numel() * operands.element_size(),
+                              _ptr(sink), sink.numel(), int(wgs_per_cu), int(iters),
+                              _DTYPE[operands.dtype], _stream(stream, operands)),
+           "pa_mfma_stream")
 
 
 def paged_kv_append(k_cache: torch.Tensor, v_cache: Optional[torch.Tensor], key: torch.Tensor,

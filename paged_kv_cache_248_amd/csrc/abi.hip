@@ -406,6 +406,21 @@ pa_status_t pa_stream_copy(const void *src, void *dst, int64_t bytes, int32_t wg
       pa::launch_stream_copy(src, dst, bytes, wgs_per_cu, static_cast<hipStream_t>(stream)));
 }
 
+pa_status_t pa_mfma_stream(const void *operands, int64_t operand_bytes, float *sink,
+                           int32_t sink_words, int32_t wgs_per_cu, int32_t iters, int32_t dtype,
+                           void *stream) {
+  if (dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
+  if (operand_bytes < 4096 || sink_words <= 0 || wgs_per_cu < 1 || wgs_per_cu > 8 || iters <= 0)
+    return PA_ERR_SHAPE;
+  if (operand_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (!operands || !sink) return PA_ERR_NULL;
+  if (!aligned16(operands)) return PA_ERR_UNSUPPORTED;
+  if (!device_ok()) return PA_ERR_DEVICE;
+  return launch_status(pa::launch_mfma_stream(operands, operand_bytes, sink, sink_words,
+                                              wgs_per_cu, iters, (pa::DType)dtype,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 pa_status_t pa_host_device_pointer(void *host_ptr, void **device_ptr) {
   if (!host_ptr || !device_ptr) return PA_ERR_NULL;
   *device_ptr = nullptr;

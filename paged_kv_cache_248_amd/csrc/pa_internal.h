@@ -121,6 +121,13 @@ hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, in
 hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes, int32_t wgs_per_cu,
                               hipStream_t stream);
 
+// Matrix-core stream: min(CUs x wgs_per_cu, sink_words) work-groups of four
+// wavefronts, each wavefront `iters` rounds of 32 v_mfma_f32_32x32x16 on
+// operands read once from `ops` (ops_bytes, a multiple of 16); work-group i
+// writes the sum of its accumulators to sink[i].
+hipError_t launch_mfma_stream(const void *ops, int64_t ops_bytes, float *sink, int32_t sink_words,
+                              int32_t wgs_per_cu, int32_t iters, DType dtype, hipStream_t stream);
+
 // Compute units of the current device (cached per device).
 int device_cu_count();
 

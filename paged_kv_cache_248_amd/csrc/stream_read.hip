@@ -1,6 +1,7 @@
 // Device read stream: the practical HBM read ceiling that the decode kernels
-// (which read K/V and write almost nothing) are compared with; and a device
-// copy stream, the read+write ceiling of the block copy and the KV append.  Every byte
+// (which read K/V and write almost nothing) are compared with; a device copy
+// stream, the read+write ceiling of the block copy and the KV append; and a
+// matrix-core stream, the practical MFMA ceiling the prefill is set beside.  Every byte
 // of the buffer is loaded once with non-temporal 16-byte loads (the kind the
 // decode kernels issue), sixteen in flight per lane, over a one-shot grid of
 // 128 work-groups per CU (the fastest of the shapes measured on MI355X:
@@ -82,6 +83,56 @@ __global__ __launch_bounds__(kStreamThreads) void stream_copy_kernel(const u32x4
   for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// Matrix-core stream: every wavefront runs `iters` rounds of 32
+// back-to-back v_mfma_f32_32x32x16 on operands it read once (eight A and
+// eight B fragments per lane, taken from the operand buffer, random 16-bit
+// data), into four independent accumulators — the matrix cores' issue rate
+// with no memory, LDS or softmax work beside it, at whatever clock the power
+// limit allows for such data.  Work-group i writes the sum of its
+// accumulators to sink[i], so nothing can be dropped.
+template <class E>
+__device__ __forceinline__ f32x16 mfma_32x32x16(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
+  if constexpr (__is_same(typename E::storage, _Float16))
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <class E>
+__global__ __launch_bounds__(kStreamThreads) void mfma_stream_kernel(const u32x4 *__restrict__ ops,
+                                                                      int64_t n16,
+                                                                      float *__restrict__ sink,
+                                                                      int iters) {
+  __shared__ float red[kStreamThreads / 64];
+  const int64_t g = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
+  u32x4 a[8], b[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    a[k] = ops[(g * 16 + k) % n16];
+    b[k] = ops[(g * 16 + 8 + k) % n16];
+  }
+  f32x16 acc[4] = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 32; ++u) acc[u & 3] = mfma_32x32x16<E>(a[u & 7], b[(u >> 2) & 7], acc[u & 3]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += acc[j][i];
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x / 64] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int w = 0; w < kStreamThreads / 64; ++w) t += red[w];
+    sink[blockIdx.x] = t;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes, int32_t wgs_per_cu,
@@ -116,6 +167,22 @@ hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, in
   profile_begin(stream);
   hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(kStreamThreads), 0, stream,
                      static_cast<const u32x4 *>(src), n16, sink);
+  profile_end(stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_stream(const void *ops, int64_t ops_bytes, float *sink, int32_t sink_words,
+                              int32_t wgs_per_cu, int32_t iters, DType dtype, hipStream_t stream) {
+  const int64_t want = (int64_t)device_cu_count() * wgs_per_cu;
+  const int grid = (int)(want < sink_words ? want : sink_words);
+  const int64_t n16 = ops_bytes / 16;
+  profile_begin(stream);
+  if (dtype == DType::F16)
+    hipLaunchKernelGGL(mfma_stream_kernel<F16>, dim3(grid), dim3(kStreamThreads), 0, stream,
+                       static_cast<const u32x4 *>(ops), n16, sink, iters);
+  else
+    hipLaunchKernelGGL(mfma_stream_kernel<BF16>, dim3(grid), dim3(kStreamThreads), 0, stream,
+                       static_cast<const u32x4 *>(ops), n16, sink, iters);
   profile_end(stream);
   return hipGetLastError();
 }

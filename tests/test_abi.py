@@ -388,3 +388,25 @@ def test_stream_copy_validation(lib):
     assert lib.pa_stream_copy(P, P2, 0, 0, None) == PA_OK
     if not gpu_available():
         assert lib.pa_stream_copy(P, P2 + 0x100000, 32, 0, None) == PA_ERR_DEVICE
+
+
+def test_mfma_stream_validation(lib):
+    f = lib.pa_mfma_stream
+    ok = dict(operands=P, nbytes=8192, sink=P2, words=16, w=1, iters=1, dtype=2)   # bf16
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["operands"], a["nbytes"], a["sink"], a["words"], a["w"], a["iters"], a["dtype"],
+                 None)
+
+    assert call(dtype=0) == PA_ERR_DTYPE            # fp32 has no such MFMA here
+    assert call(dtype=7) == PA_ERR_DTYPE
+    assert call(nbytes=2048) == PA_ERR_SHAPE
+    assert call(words=0) == PA_ERR_SHAPE
+    assert call(w=0) == PA_ERR_SHAPE
+    assert call(w=9) == PA_ERR_SHAPE
+    assert call(iters=0) == PA_ERR_SHAPE
+    assert call(nbytes=8200) == PA_ERR_UNSUPPORTED
+    assert call(operands=None) == PA_ERR_NULL
+    assert call(sink=None) == PA_ERR_NULL
+    assert call(operands=P + 8) == PA_ERR_UNSUPPORTED
