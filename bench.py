@@ -34,18 +34,15 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16/fp16 matrix peak
 
 METRIC = "paged decode KV GB/s (% of 8 TB/s HBM peak); prefill TFLOP/s (% MFMA peak)"
 
-# Sources of the decode kernel: the traffic figure is only reported while
-# these match the version the counters were collected on.
 # Sources of each kernel: a kernel's HBM traffic figure (profiles/hbm_traffic.md)
 # is only reported while these match the version the counters were taken on.
 _CSRC = "paged_kv_cache_248_amd/csrc/"
 SOURCES = {
     "decode": [_CSRC + "decode.hip", _CSRC + "pa_device.h"],
-    "prefill": [_CSRC + "prefill.hip", _CSRC + "pa_device.h"],
+    "prefill": [_CSRC + "prefill.hip", _CSRC + "prefill_common.h", _CSRC + "pa_device.h"],
     "copy": [_CSRC + "copy_blocks.hip", _CSRC + "pa_device.h"],
     "append": [_CSRC + "append.hip", _CSRC + "pa_device.h"],
 }
-DECODE_SOURCES = SOURCES["decode"]
 
 
 def log(msg: str) -> None:
@@ -160,14 +157,16 @@ def bench_decode(pa, torch, wl, case, steps, warmup):
     }
 
 
-def bench_prefill(pa, torch, wl, case, steps, warmup):
+def bench_prefill(pa, torch, wl, case, steps, warmup, kernel="pingpong"):
+    """kernel: "pingpong" (paged_attn_prefill) or "halftile"
+    (paged_attn_prefill_halftile, the second schedule, for comparison)."""
     kv = case.kv
     out = torch.empty_like(case.query)
+    fn = pa.paged_attn_prefill if kernel == "pingpong" else pa.paged_attn_prefill_halftile
 
     def step():
-        pa.paged_attn_prefill(out, case.query, kv.k_cache, kv.v_cache, kv.block_tables,
-                              kv.context_lens, case.query_start_loc, case.scale,
-                              case.max_query_len, kv.max_context_len)
+        fn(out, case.query, kv.k_cache, kv.v_cache, kv.block_tables, kv.context_lens,
+           case.query_start_loc, case.scale, case.max_query_len, kv.max_context_len)
 
     timer = KernelTimer(pa, torch, steps)
     ms = timed_steps(torch, step, steps, warmup, timer)
@@ -183,8 +182,8 @@ def bench_prefill(pa, torch, wl, case, steps, warmup):
     # of every (sequence, kv head) read once
     hbm_bytes = 2 * T * Hq * D * e + 2 * int(ctx.sum()) * Hkv * D * e
     return {
-        "workload": case.name, "ms_per_step": ms, "kernel_ms": kms, "flops": flops,
-        "hbm_bytes": hbm_bytes,
+        "workload": case.name, "kernel": kernel, "ms_per_step": ms, "kernel_ms": kms,
+        "flops": flops, "hbm_bytes": hbm_bytes,
         "TFLOPs": flops / (ms * 1e-3) / 1e12, "kernel_TFLOPs": flops / (kms * 1e-3) / 1e12,
         "frac_mfma_peak": flops / (kms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
         "tokens_per_s": T / (ms * 1e-3), "num_seqs": len(ctx), "new_tokens": int(T),
@@ -705,6 +704,7 @@ def main() -> int:
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--only", default=None, choices=["llama7b_decode_f16", "gqa_decode_bf16",
                                                        "long_decode_f16", "prefill_bf16",
+                                                       "prefill_bf16_halftile",
                                                        "copy_bf16", "append_bf16", "swap_bf16",
                                                        "stream_copy", "stream_copy_lib", "stream_read",
                                                        "mfma_stream", "prefill_unfused_bf16",
@@ -759,6 +759,12 @@ def main() -> int:
                                   max(2, args.warmup // 100))
         print(json.dumps(r), flush=True)
         return 0
+    if args.only == "prefill_bf16_halftile":
+        log("generating prefill_bf16 ...")
+        case = wl.prefill_bf16(device=dev)
+        r = bench_prefill(pa, torch, wl, case, args.steps, args.warmup, kernel="halftile")
+        print(json.dumps(r), flush=True)
+        return 0
     if args.only:
         log(f"generating {args.only} ...")
         case = wl.WORKLOADS[args.only](device=dev)
@@ -802,6 +808,11 @@ def main() -> int:
         r = bench_prefill(pa, torch, wl, pc, args.steps, args.warmup)
         log(f"  prefill: {r['ms_per_step']:.3f} ms/step, {r['kernel_TFLOPs']:.0f} TFLOP/s")
         extra["prefill_bf16"] = r
+        h = bench_prefill(pa, torch, wl, pc, args.steps, args.warmup, kernel="halftile")
+        h["vs_pingpong"] = h["kernel_TFLOPs"] / r["kernel_TFLOPs"]
+        log(f"  prefill, half-tile schedule: {h['kernel_TFLOPs']:.0f} TFLOP/s "
+            f"({h['vs_pingpong']:.3f} of the ping-pong kernel)")
+        extra["prefill_bf16_halftile"] = h
         u = bench_prefill_unfused(pa, torch, wl, pc, max(3, args.steps // 10),
                                   max(2, args.warmup // 100))
         u["fused_speedup"] = u["ms_per_step"] / r["ms_per_step"]

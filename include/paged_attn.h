@@ -9,8 +9,10 @@
  *   paged_kv_copy_blocks  copies whole cache blocks between two pools by a
  *                         src_to_dst mapping.
  * Beside them: paged_kv_append (writes new tokens' K/V into their slots), a
- * host block manager (pa_bm_*) that produces block tables, and
- * paged_attn_prefill_unfused, the unfused baseline of prefill.
+ * host block manager (pa_bm_*) that produces block tables,
+ * paged_attn_prefill_unfused, the unfused baseline of prefill, and
+ * paged_attn_prefill_halftile, the same prefill with a second kernel
+ * schedule for comparison.
  *
  * Pages the operations follow (cited by title):
  *   [P-swap] "vLLM中FlashAttention与KVCache交换机制解析"
@@ -206,6 +208,28 @@ pa_status_t paged_attn_prefill(void *out, const void *query, const void *k_cache
                                int32_t block_size, int32_t num_blocks,
                                int32_t max_blocks_per_seq, float scale, int32_t dtype,
                                void *stream);
+
+/* --------------------------------------------------------------------------
+ * The same causal paged prefill with a second kernel schedule.
+ *
+ * Computes exactly what paged_attn_prefill computes (same arguments, same
+ * layouts, same validation and status codes, no workspace) with the
+ * half-tile schedule: each wavefront interleaves tile j+1's QK^T with tile
+ * j's softmax and PV, instead of paged_attn_prefill's ping-pong of two
+ * wavefront groups.  Kept so that the two schedules can be measured against
+ * each other on one GPU; paged_attn_prefill, the faster of the two on
+ * MI355X, is the one to call.
+ * ------------------------------------------------------------------------ */
+pa_status_t paged_attn_prefill_halftile(void *out, const void *query, const void *k_cache,
+                                        const void *v_cache, const int32_t *block_tables,
+                                        const int32_t *context_lens,
+                                        const int32_t *query_start_loc, int32_t num_seqs,
+                                        int32_t total_query_tokens, int32_t max_query_len,
+                                        int32_t max_context_len, int32_t num_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t num_blocks,
+                                        int32_t max_blocks_per_seq, float scale, int32_t dtype,
+                                        void *stream);
 
 /* --------------------------------------------------------------------------
  * Unfused causal paged prefill (baseline).

@@ -19,7 +19,8 @@ __all__ = [
     "PagedAttnError", "library_path", "load_library",
     "paged_attn_decode", "paged_attn_decode_workspace_size", "paged_attn_decode_noalloc",
     "DECODE_NOALLOC_SCRATCH_BYTES",
-    "paged_attn_prefill", "paged_attn_prefill_unfused", "paged_attn_prefill_unfused_workspace_size",
+    "paged_attn_prefill", "paged_attn_prefill_halftile",
+    "paged_attn_prefill_unfused", "paged_attn_prefill_unfused_workspace_size",
     "paged_kv_copy_blocks", "paged_kv_copy_blocks_workspace_size",
     "paged_kv_append", "BlockManager", "OutOfBlocksError",
     "DEFAULT_PARTITION", "DEFAULT_PARTITION_GQA", "default_partition",
@@ -55,6 +56,9 @@ _SIGS = {
     "paged_attn_prefill": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32,
                                            _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                            ctypes.c_float, ctypes.c_int, _VP]),
+    "paged_attn_prefill_halftile": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32,
+                                                    _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                    _I32, ctypes.c_float, ctypes.c_int, _VP]),
     "paged_attn_prefill_unfused_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32,
                                                         ctypes.c_int]),
     "paged_attn_prefill_unfused": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32,
@@ -247,6 +251,22 @@ def paged_attn_prefill(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Te
     query/out [T, Hq, D]; query_start_loc int32 [B+1]; context_lens int32 [B]
     counts prefix + new keys (all already in the cache).
     """
+    return _prefill("paged_attn_prefill", out, query, k_cache, v_cache, block_tables,
+                    context_lens, query_start_loc, scale, max_query_len, max_context_len, stream)
+
+
+def paged_attn_prefill_halftile(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor,
+                                v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                context_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                                scale: float, max_query_len: int, max_context_len: int,
+                                stream=None) -> torch.Tensor:
+    """The same prefill with the library's second (half-tile) kernel schedule."""
+    return _prefill("paged_attn_prefill_halftile", out, query, k_cache, v_cache, block_tables,
+                    context_lens, query_start_loc, scale, max_query_len, max_context_len, stream)
+
+
+def _prefill(name, out, query, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+             scale, max_query_len, max_context_len, stream):
     lib = load_library()
     _need(query, "query", dims=3)
     dt = query.dtype
@@ -264,12 +284,12 @@ def paged_attn_prefill(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Te
     if (Dk != D or out.shape != query.shape or v_cache.shape != k_cache.shape
             or block_tables.shape[0] != B or query_start_loc.shape[0] != B + 1):
         raise ValueError("inconsistent shapes")
-    st = lib.paged_attn_prefill(_ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache),
-                                _ptr(block_tables), _ptr(context_lens), _ptr(query_start_loc),
-                                B, T, int(max_query_len), int(max_context_len), Hq, Hkv, D, bs,
-                                nblk, block_tables.shape[1], float(scale), _DTYPE[dt],
-                                _stream(stream, query))
-    _check(st, "paged_attn_prefill")
+    st = getattr(lib, name)(_ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache),
+                            _ptr(block_tables), _ptr(context_lens), _ptr(query_start_loc),
+                            B, T, int(max_query_len), int(max_context_len), Hq, Hkv, D, bs,
+                            nblk, block_tables.shape[1], float(scale), _DTYPE[dt],
+                            _stream(stream, query))
+    _check(st, name)
     return out
 
 

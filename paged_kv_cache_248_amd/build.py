@@ -27,7 +27,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedattn.so")
 SOURCES = ["abi.hip", "append.hip", "block_manager.cpp", "copy_blocks.hip", "decode.hip",
-           "prefill.hip", "stream_read.hip", "unfused.hip"]
+           "prefill.hip", "prefill_halftile.hip", "stream_read.hip", "unfused.hip"]
 # the unfused prefill baseline calls hipBLASLt for its two matrix products
 LIBS = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")

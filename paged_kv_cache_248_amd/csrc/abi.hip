@@ -206,14 +206,16 @@ pa_status_t paged_attn_decode_noalloc(void *out, const void *query, const void *
                      nullptr, 0, stream);
 }
 
-pa_status_t paged_attn_prefill(void *out, const void *query, const void *k_cache,
-                               const void *v_cache, const int32_t *block_tables,
-                               const int32_t *context_lens, const int32_t *query_start_loc,
-                               int32_t num_seqs, int32_t total_query_tokens,
-                               int32_t max_query_len, int32_t max_context_len, int32_t num_heads,
-                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                               int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
-                               int32_t dtype, void *stream) {
+namespace {
+
+pa_status_t prefill_call(void *out, const void *query, const void *k_cache, const void *v_cache,
+                         const int32_t *block_tables, const int32_t *context_lens,
+                         const int32_t *query_start_loc, int32_t num_seqs,
+                         int32_t total_query_tokens, int32_t max_query_len,
+                         int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                         int32_t max_blocks_per_seq, float scale, int32_t dtype, bool halftile,
+                         void *stream) {
   if (dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
   if (!(scale > 0.0f) || !std::isfinite(scale)) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || total_query_tokens < 0 || max_query_len < 0 || max_context_len < 0 ||
@@ -253,7 +255,40 @@ pa_status_t paged_attn_prefill(void *out, const void *query, const void *k_cache
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.scale = scale;
   a.dtype = (pa::DType)dtype;
-  return launch_status(pa::launch_prefill(a, static_cast<hipStream_t>(stream)));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return launch_status(halftile ? pa::launch_prefill_halftile(a, st) : pa::launch_prefill(a, st));
+}
+
+}  // namespace
+
+pa_status_t paged_attn_prefill(void *out, const void *query, const void *k_cache,
+                               const void *v_cache, const int32_t *block_tables,
+                               const int32_t *context_lens, const int32_t *query_start_loc,
+                               int32_t num_seqs, int32_t total_query_tokens,
+                               int32_t max_query_len, int32_t max_context_len, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
+                               int32_t dtype, void *stream) {
+  return prefill_call(out, query, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                      num_seqs, total_query_tokens, max_query_len, max_context_len, num_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, scale,
+                      dtype, false, stream);
+}
+
+pa_status_t paged_attn_prefill_halftile(void *out, const void *query, const void *k_cache,
+                                        const void *v_cache, const int32_t *block_tables,
+                                        const int32_t *context_lens,
+                                        const int32_t *query_start_loc, int32_t num_seqs,
+                                        int32_t total_query_tokens, int32_t max_query_len,
+                                        int32_t max_context_len, int32_t num_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t num_blocks,
+                                        int32_t max_blocks_per_seq, float scale, int32_t dtype,
+                                        void *stream) {
+  return prefill_call(out, query, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                      num_seqs, total_query_tokens, max_query_len, max_context_len, num_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, scale,
+                      dtype, true, stream);
 }
 
 size_t paged_attn_prefill_unfused_workspace_size(int32_t max_query_len, int32_t max_context_len,

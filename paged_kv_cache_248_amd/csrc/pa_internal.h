@@ -56,6 +56,8 @@ struct PrefillLaunch {
 };
 
 hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t stream);
+// The same prefill with the half-tile schedule (prefill_halftile.hip).
+hipError_t launch_prefill_halftile(const PrefillLaunch &a, hipStream_t stream);
 
 struct CopyLaunch {
   const void *src_k, *src_v;

@@ -48,118 +48,13 @@
 //     work-groups of an XCD walk one (sequence, kv head) pair at a time
 //     through all its query tiles (the last, with the most keys, first), so
 //     the tiles sharing K/V run together in one L2.
-#include <algorithm>
-#include <atomic>
-#include <type_traits>
-#include <utility>
-
-#include "pa_device.h"
-#include "pa_internal.h"
+#include "prefill_common.h"
 
 namespace pa {
 
 namespace {
 
-constexpr int kBN = 64;        // keys per tile
-constexpr int kRows = 32;      // query rows per wavefront
-constexpr int kWaves = 8;      // two groups of four
-constexpr int kStages = 4;     // LDS stages per K and per V tile stream
 constexpr int kReadAhead = 7;  // MFMAs whose operand reads are in flight ahead of the current one
-constexpr int kXcds = 8;       // XCDs of an MI355X; work-group ids are dealt to them round-robin
-
-struct PrefillParams {
-  void *out;
-  const void *query;
-  const void *k_cache;
-  const void *v_cache;
-  const int32_t *block_tables;
-  const int32_t *context_lens;
-  const int32_t *query_start_loc;
-  int32_t num_heads, num_kv_heads, group, heads_per_wg, subgroups, pos_per_wg;
-  int32_t bs_log2, max_blocks_per_seq, num_blocks, ctx_cap, num_seqs;
-  int32_t num_pairs, num_qtiles;
-  float scale_log2e;
-};
-
-template <class E>
-__device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
-  if constexpr (__is_same(typename E::storage, _Float16))
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-
-// V^T tile layout.  Row d holds the tile's 64 keys; inside every group of 16
-// keys the key order is k -> (k & 3) | bit3(k) << 2 | bit2(k) << 3, which puts
-// the 8 keys one lane feeds to a PV k-step (keys 4h..4h+3 and 8+4h..8+4h+3
-// for lane half h) in one contiguous 16-byte chunk.  Chunk c of row d is
-// stored at c ^ vt_swz(d); the swizzle depends on d mod 32 only, so the
-// operand reads of every 32-row sub-tile share one set of per-lane offsets,
-// and is conflict-free for those reads.
-__device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) & 7) ^ ((d >> 4) & 1); }
-
-__device__ __forceinline__ float max3(float a, float b, float c) {
-  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
-}
-
-// Maximum over a lane's 32 scores and those of the lane 32 apart (the two
-// halves of one query's keys), as a depth-4 tree of 3-input maxima; the
-// halves are exchanged with v_permlane32_swap.  NaN-propagating maximum:
-// lowers to v_maximum3_f32 without the per-operand canonicalisation of IEEE
-// fmax.
-__device__ __forceinline__ float row_max(const f32x16 (&s)[2]) {
-  float a[11];
-#pragma unroll
-  for (int i = 0; i < 10; ++i) {
-    const int x = 3 * i, y = 3 * i + 1, z = 3 * i + 2;
-    a[i] = max3(s[x >> 4][x & 15], s[y >> 4][y & 15], s[z >> 4][z & 15]);
-  }
-  a[10] = __builtin_elementwise_maximum(s[1][14], s[1][15]);
-  const float b0 = max3(a[0], a[1], a[2]), b1 = max3(a[3], a[4], a[5]);
-  const float b2 = max3(a[6], a[7], a[8]), b3 = __builtin_elementwise_maximum(a[9], a[10]);
-  const float r = __builtin_elementwise_maximum(max3(b0, b1, b2), b3);
-  const f32x2 sw = pair_xor32(r);
-  return __builtin_elementwise_maximum(sw[0], sw[1]);
-}
-
-// Raise the running maximum (and rescale O and L) only when a tile's maximum
-// exceeds it by more than 2^kLazy; weights then stay within [0, 2^kLazy].
-constexpr float kLazy = 8.0f;
-
-// Work-group barrier between phases.  It keeps the compiler from moving
-// memory accesses or any other instruction across it and waits for nothing:
-// every LDS read of the loop is consumed (so complete) before its phase ends,
-// LDS is written only by the direct-to-LDS tile loads, whose completion is
-// awaited explicitly with exact counts before the barrier that publishes a
-// tile, and block-id scalar loads may stay in flight across it.
-__device__ __forceinline__ void phase_sync() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// s_waitcnt lgkmcnt(N), tied to the registers it makes valid so that their
-// users stay after it.
-template <int N>
-__device__ __forceinline__ void lds_tie(u32x4 (&r)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) : "i"(N));
-}
-
-
-// Scalar load of base[idx] (idx uniform), issued where it stands; its value
-// may be used only after sload_tie.  Block-table entries are read this way so
-// that the compiler can neither move the load next to its use (where the
-// wait would also stall the in-flight LDS reads) nor wait on it early.
-__device__ __forceinline__ int sload(const int32_t *base, int idx) {
-  int v;
-  asm volatile("s_load_dword %0, %1, %2" : "=s"(v) : "s"(base), "s"(idx * 4) : "memory");
-  return v;
-}
 
 template <class E, int D>
 __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
@@ -564,54 +459,15 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
 template <class E, int D>
 hipError_t launch_typed(const PrefillLaunch &a, hipStream_t stream) {
   PrefillParams p;
-  p.out = a.out;
-  p.query = a.query;
-  p.k_cache = a.k_cache;
-  p.v_cache = a.v_cache;
-  p.block_tables = a.block_tables;
-  p.context_lens = a.context_lens;
-  p.query_start_loc = a.query_start_loc;
-  p.num_heads = a.num_heads;
-  p.num_kv_heads = a.num_kv_heads;
-  p.group = a.num_heads / a.num_kv_heads;
-  p.heads_per_wg = (p.group % 4 == 0) ? 4 : (p.group % 2 == 0) ? 2 : 1;
-  p.subgroups = p.group / p.heads_per_wg;
-  p.pos_per_wg = kRows * (kWaves / p.heads_per_wg);
-  int bl = 0;
-  while ((1 << bl) < a.block_size) ++bl;
-  p.bs_log2 = bl;
-  p.max_blocks_per_seq = a.max_blocks_per_seq;
-  p.num_blocks = a.num_blocks;
-  p.ctx_cap = a.ctx_cap;
-  p.num_seqs = a.num_seqs;
-  p.scale_log2e = a.scale * kLog2e;
-  const long long pairs = (long long)a.num_seqs * a.num_kv_heads * p.subgroups;
-  const long long qtiles = (a.max_query_len + p.pos_per_wg - 1) / p.pos_per_wg;
-  // Items of the XCD with the most; one work-group per CU at most.
-  const long long xcd_items = ((pairs + kXcds - 1) / kXcds) * qtiles;
-  if (xcd_items > 0x7fffffffLL) return hipErrorInvalidValue;
-  int cus = 0, dev = 0;
-  {
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-  }
-  const long long grid = kXcds * std::min<long long>(std::max(cus / kXcds, 1), xcd_items);
-  p.num_pairs = (int32_t)pairs;
-  p.num_qtiles = (int32_t)qtiles;
-  const size_t lds_bytes = (size_t)2 * kStages * 64 * D * 2;
-  // The LDS attribute belongs to the function on one device: bit d of this
-  // per-instantiation mask records that device d has it (devices past 63 set
-  // it on every call).
+  long long grid = 0;
+  int dev = 0;
+  hipError_t e = prefill_setup(a, p, grid, dev);
+  if (e != hipSuccess) return e;
+  const size_t lds_bytes = (size_t)2 * kStages * kBN * D * 2;
   static std::atomic<uint64_t> attr_devices{0};
-  const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t{1} << dev : 0;
-  if (bit == 0 || (attr_devices.load(std::memory_order_relaxed) & bit) == 0) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_kernel<E, D>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)lds_bytes);
-    if (e != hipSuccess) return e;
-    attr_devices.fetch_or(bit, std::memory_order_relaxed);
-  }
+  e = prefill_allow_lds(reinterpret_cast<const void *>(&prefill_kernel<E, D>), lds_bytes, dev,
+                        attr_devices);
+  if (e != hipSuccess) return e;
   profile_begin(stream);
   hipLaunchKernelGGL((prefill_kernel<E, D>), dim3((unsigned)grid), dim3(64 * kWaves), lds_bytes,
                      stream, p);

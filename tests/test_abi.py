@@ -127,13 +127,16 @@ def test_decode_default_partition_depends_on_group(lib):
     assert pa.default_partition(32, 32) == pa.DEFAULT_PARTITION == 512
 
 
-def _prefill(lib, **kw):
+def _prefill(lib, entry="paged_attn_prefill", **kw):
     a = dict(out=P, query=P, k=P, v=P, bt=P, cl=P, qsl=P2, B=2, T=10, maxq=8, maxctx=40, Hq=8,
              Hkv=2, D=128, bs=16, nblk=64, mbps=8, scale=0.125, dtype=2, stream=None)
     a.update(kw)
-    return lib.paged_attn_prefill(a["out"], a["query"], a["k"], a["v"], a["bt"], a["cl"], a["qsl"],
-                                  a["B"], a["T"], a["maxq"], a["maxctx"], a["Hq"], a["Hkv"], a["D"],
-                                  a["bs"], a["nblk"], a["mbps"], a["scale"], a["dtype"], a["stream"])
+    return getattr(lib, entry)(a["out"], a["query"], a["k"], a["v"], a["bt"], a["cl"], a["qsl"],
+                               a["B"], a["T"], a["maxq"], a["maxctx"], a["Hq"], a["Hkv"], a["D"],
+                               a["bs"], a["nblk"], a["mbps"], a["scale"], a["dtype"], a["stream"])
+
+
+PREFILL_ENTRIES = ["paged_attn_prefill", "paged_attn_prefill_halftile"]
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -152,14 +155,16 @@ def _prefill(lib, **kw):
     (dict(T=0), PA_OK),
     (dict(B=0), PA_OK),
 ])
-def test_prefill_validation(lib, kw, want):
-    assert _prefill(lib, **kw) == want
+@pytest.mark.parametrize("entry", PREFILL_ENTRIES)
+def test_prefill_validation(lib, kw, want, entry):
+    assert _prefill(lib, entry, **kw) == want
 
 
-def test_prefill_reports_missing_device(lib):
+@pytest.mark.parametrize("entry", PREFILL_ENTRIES)
+def test_prefill_reports_missing_device(lib, entry):
     if gpu_available():
         pytest.skip("a GPU is present: valid arguments would launch")
-    assert _prefill(lib) == PA_ERR_DEVICE
+    assert _prefill(lib, entry) == PA_ERR_DEVICE
 
 
 def _copy(lib, **kw):

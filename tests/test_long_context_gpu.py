@@ -98,8 +98,9 @@ def test_decode_planted_keys_long_context(dtype, Hq, Hkv, bs, part):
         f"max err / row max|ref| {rel_to_row_max(got, ref):.3e}, max|ref| {np.abs(ref).max():.2f}")
 
 
+@pytest.mark.parametrize("kernel", ["pingpong", "halftile"])
 @pytest.mark.parametrize("dtype,bs", [("bf16", 16), ("f16", 32)])
-def test_prefill_planted_keys_long_context(dtype, bs):
+def test_prefill_planted_keys_long_context(dtype, bs, kernel):
     """Prefixes of 30000 and 16000 tokens: planted keys for chosen query rows
     across the whole visible range (the first key, the row's own position, the
     key just before it, random keys), so each key tile's contribution to those
@@ -130,9 +131,9 @@ def test_prefill_planted_keys_long_context(dtype, bs):
     # key wins where two name the same position)
     plant(kv, rows_q, row_seq, pos, G, sc)
     out = torch.full_like(case.query, float("nan"))
-    pa.paged_attn_prefill(out, case.query, kv.k_cache, kv.v_cache, kv.block_tables,
-                          kv.context_lens, case.query_start_loc, case.scale, case.max_query_len,
-                          kv.max_context_len)
+    fn = pa.paged_attn_prefill if kernel == "pingpong" else pa.paged_attn_prefill_halftile
+    fn(out, case.query, kv.k_cache, kv.v_cache, kv.block_tables, kv.context_lens,
+       case.query_start_loc, case.scale, case.max_query_len, kv.max_context_len)
     torch.cuda.synchronize()
     got_all = host(out)
     k, v, tables, cl = compact_pool(kv, [0, 1])
