@@ -328,7 +328,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
       // on this SIMD); rounding P to 16 bits for PV is unbiased, so the
       // normalised output differs from summing the rounded weights only by
       // that rounding noise.
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+      float ls[4];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
           for (int q = 0; q < 4; ++q) {
             const float e0 = fast_exp2(fmaf(s[kt][8 * hh + 2 * q], c, nm));
             const float e1 = fast_exp2(fmaf(s[kt][8 * hh + 2 * q + 1], c, nm));
-            ls[q] += e0 + e1;
+            ls[q] = kt == 0 && hh == 0 ? e0 + e1 : ls[q] + (e0 + e1);
             w[q] = pack2<E>(e0, e1);
           }
           pf[2 * kt + hh] = w;
