@@ -78,7 +78,7 @@ typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } pa_dtype_
  * tile then feeds several heads, and longer partitions cut the per-item
  * overhead; measured fastest on the GQA workload), else PA_DEFAULT_PARTITION. */
 #define PA_DEFAULT_PARTITION 512
-#define PA_DEFAULT_PARTITION_GQA 2048
+#define PA_DEFAULT_PARTITION_GQA 4096
 /* Most partitions one decode sequence may be split into
  * (ceil(min(max_context_len, max_blocks_per_seq*block_size) / partition)). */
 #define PA_MAX_PARTITIONS 2048

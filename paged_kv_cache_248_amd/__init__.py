@@ -28,7 +28,7 @@ __all__ = [
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 DEFAULT_PARTITION = 512       # PA_DEFAULT_PARTITION
-DEFAULT_PARTITION_GQA = 2048  # PA_DEFAULT_PARTITION_GQA
+DEFAULT_PARTITION_GQA = 4096  # PA_DEFAULT_PARTITION_GQA
 DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20   # PA_DECODE_NOALLOC_SCRATCH_BYTES
 
 

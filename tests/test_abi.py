@@ -115,15 +115,15 @@ def test_decode_workspace_size(lib):
 
 
 def test_decode_default_partition_depends_on_group(lib):
-    """partition_size 0 picks 2048 tokens for 4+ heads per kv head, else 512."""
+    """partition_size 0 picks 4096 tokens for 4+ heads per kv head, else 512."""
     import paged_kv_cache_248_amd as pa
     ws = lib.paged_attn_decode_workspace_size
     # group 4 (8 heads, 2 kv heads)
-    assert ws(4, 8, 2, 128, 8192, 0) == ws(4, 8, 2, 128, 8192, 2048) != ws(4, 8, 2, 128, 8192, 1024)
+    assert ws(4, 8, 2, 128, 16384, 0) == ws(4, 8, 2, 128, 16384, 4096) != ws(4, 8, 2, 128, 16384, 2048)
     # group 2 and MHA
     assert ws(4, 8, 4, 128, 4096, 0) == ws(4, 8, 4, 128, 4096, 512) != ws(4, 8, 4, 128, 4096, 1024)
     assert ws(4, 8, 8, 128, 4096, 0) == ws(4, 8, 8, 128, 4096, 512)
-    assert pa.default_partition(8, 2) == 2048 and pa.default_partition(8, 4) == 512
+    assert pa.default_partition(8, 2) == 4096 and pa.default_partition(8, 4) == 512
     assert pa.default_partition(32, 32) == pa.DEFAULT_PARTITION == 512
 
 

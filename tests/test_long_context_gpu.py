@@ -58,7 +58,8 @@ def rel_to_row_max(got, ref):
 
 @pytest.mark.parametrize("dtype,Hq,Hkv,bs,part", [
     ("f16", 32, 32, 32, 512),      # the long-context workload's shape and partitions
-    ("bf16", 32, 8, 16, 2048),     # GQA on the matrix-core kernel, default partitions
+    ("bf16", 32, 8, 16, 4096),     # GQA on the matrix-core kernel, default partitions
+    ("bf16", 32, 8, 16, 2048),
     ("bf16", 32, 8, 16, 512),
 ])
 def test_decode_planted_keys_long_context(dtype, Hq, Hkv, bs, part):

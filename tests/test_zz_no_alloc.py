@@ -36,7 +36,7 @@ def _args(case):
 @pytest.mark.parametrize("dtype,Hq,Hkv,part", [
     ("f16", 32, 32, 512),       # vector-ALU kernel, split into partitions + merge
     ("bf16", 32, 8, 512),       # matrix-core GQA kernel, split + merge
-    ("bf16", 32, 8, 0),         # library default partition (2048): mostly one partition
+    ("bf16", 32, 8, 0),         # library default partition (4096): mostly one partition
     ("f32", 8, 4, 256),
 ])
 def test_noalloc_matches_workspace_decode_on_consecutive_calls(dtype, Hq, Hkv, part):
