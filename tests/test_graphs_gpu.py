@@ -69,16 +69,18 @@ def test_split_gqa_decode_graph_replays_match_eager():
     log(f"split GQA decode: {REPLAYS} replays bit-identical to eager")
 
 
-def test_prefill_graph_replays_match_eager():
+@pytest.mark.parametrize("kernel", ["pingpong", "halftile"])
+def test_prefill_graph_replays_match_eager(kernel):
     case = wl.make_prefill([0, 200, 35], [130, 64, 7], 16, 4, 128, 16, "bf16", seed=42,
                            device=DEV)
     kv = case.kv
     maxq, maxctx = case.max_query_len, kv.max_context_len
     out = torch.empty_like(case.query)
+    fn = pa.paged_attn_prefill if kernel == "pingpong" else pa.paged_attn_prefill_halftile
 
     def call(o):
-        pa.paged_attn_prefill(o, case.query, kv.k_cache, kv.v_cache, kv.block_tables,
-                              kv.context_lens, case.query_start_loc, case.scale, maxq, maxctx)
+        fn(o, case.query, kv.k_cache, kv.v_cache, kv.block_tables, kv.context_lens,
+           case.query_start_loc, case.scale, maxq, maxctx)
 
     g = capture(lambda: call(out))
     gen = torch.Generator(device="cpu").manual_seed(42)
@@ -94,7 +96,7 @@ def test_prefill_graph_replays_match_eager():
     ref = prefill_ref(host(case.query), host(kv.k_cache), host(kv.v_cache),
                       host(kv.block_tables), host(kv.context_lens), host(case.query_start_loc),
                       case.scale)
-    assert_close(host(out), ref, "bf16", "prefill graph")
+    assert_close(host(out), ref, "bf16", f"prefill graph ({kernel})")
 
 
 def test_append_graph_replays_match_eager():
