@@ -18,12 +18,15 @@
 //     packed [tokens, kv_heads, head_dim] inputs); each lane moves one
 //     16-byte piece of every one of them (the K and V rows of a token are
 //     2 * kv_heads * head_dim * elem / 16 pieces).  A lane first issues its
-//     8 loads (they depend on nothing); meanwhile the first wavefront finds
-//     the 8 destinations on the scalar unit (one binary search of
-//     query_start_loc, then context_lens and the block table through scalar
-//     loads, whose counter is separate from the vector loads in flight) and
-//     publishes them in LDS; after one barrier every lane stores.  Rows are
-//     read and written once, with non-temporal accesses;
+//     8 loads (they depend on nothing); meanwhile lanes 0-7 of the first
+//     wavefront find the 8 destinations side by side, one token each (a
+//     binary search of query_start_loc, then context_lens and the block
+//     table), and publish them in LDS; after one barrier every lane stores.
+//     The destinations cost a handful of dependent loads; one lane walking
+//     the 8 tokens through scalar loads took some thirty, and the stores,
+//     which wait for them, started that much later (4.6 against 5.1 TB/s on
+//     the 134 MB append workload).  Rows are read and written once, with
+//     non-temporal accesses;
 //   * a token with no valid destination (position before 0 or past the table
 //     row, or a table entry outside the pool) is skipped: nothing outside the
 //     named slots is ever written.
@@ -52,9 +55,6 @@ __device__ __forceinline__ u32x4 ldnt(const char *p) {
 __device__ __forceinline__ void stnt(char *p, u32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
 }
-
-typedef const __attribute__((address_space(4))) int32_t cint32;
-__device__ __forceinline__ cint32 *as_const(const int32_t *p) { return (cint32 *)(p); }
 
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   constexpr int NT = kTokensPerGroup;
@@ -99,33 +99,31 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   u32x4 v[NT];
   const int c0 = threadIdx.x;
   if (c0 < per_token) load(c0, v);
-  // Destinations, on the scalar unit of the first wavefront: row index
-  // (block, kv head 0, slot) in units of head rows, or -1 for none.
+  // Destinations: row index (block, kv head 0, slot) in units of head rows,
+  // or -1 for none.
   if (threadIdx.x < 64) {
-    cint32 *qsl = as_const(p.query_start_loc);
-    int lo = 0, hi = p.num_seqs;                // qsl[lo] <= t_begin < qsl[hi]
+    // lane k < NT: token t_begin + k, its sequence by a binary search of
+    // query_start_loc, then its slot; the NT searches run side by side
+    const int lane = threadIdx.x;
+    const int t = t_begin + min(lane, NT - 1);
+    const int32_t *qsl = p.query_start_loc;
+    int lo = 0, hi = p.num_seqs;                // qsl[lo] <= t < qsl[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (qsl[mid] <= t_begin) lo = mid;
+      if (qsl[mid] <= t) lo = mid;
       else hi = mid;
     }
-    int b = lo;
+    const int b = lo;
     const int cap = p.max_blocks_per_seq << p.bs_log2;
-    for (int k = 0; k < NT; ++k) {
-      long long row = -1;
-      const int t = t_begin + k;
-      if (k < n_tok) {
-        while (b + 1 < p.num_seqs && qsl[b + 1] <= t) ++b;
-        const int q_b = qsl[b + 1] - qsl[b];
-        const int pos = as_const(p.context_lens)[b] - q_b + (t - qsl[b]);
-        if (pos >= 0 && pos < cap) {
-          const int blk = as_const(p.block_tables)[(size_t)b * p.max_blocks_per_seq + (pos >> p.bs_log2)];
-          if (blk >= 0 && blk < p.num_blocks)
-            row = (long long)blk * p.num_kv_heads * bs + (pos & (bs - 1));
-        }
-      }
-      if (threadIdx.x == 0) s_row[k] = row;
+    const int q0 = qsl[b], q1 = qsl[b + 1];
+    const int pos = p.context_lens[b] - (q1 - q0) + (t - q0);
+    long long row = -1;
+    if (lane < n_tok && pos >= 0 && pos < cap) {
+      const int blk = p.block_tables[(size_t)b * p.max_blocks_per_seq + (pos >> p.bs_log2)];
+      if (blk >= 0 && blk < p.num_blocks)
+        row = (long long)blk * p.num_kv_heads * bs + (pos & (bs - 1));
     }
+    if (lane < NT) s_row[lane] = row;
   }
   __syncthreads();
   if (c0 < per_token) store(c0, v);
