@@ -95,6 +95,19 @@ def test_append_empty_sequences_between_work_group_runs():
     check_case(case, "empty sequences")
 
 
+def test_append_long_runs_of_empty_sequences():
+    """700 sequences, most of them empty, with runs of up to 200 empty ones
+    inside one 8-token run: each token's sequence is found by its own search
+    of a long query_start_loc."""
+    rng = np.random.default_rng(71)
+    new = np.zeros(700, dtype=np.int64)
+    new[[0, 3, 204, 205, 206, 420, 421, 699]] = [1, 2, 1, 1, 3, 9, 1, 5]
+    new[rng.choice(np.arange(430, 690), 40, replace=False)] = rng.integers(1, 4, 40)
+    pre = rng.integers(0, 40, new.size)
+    case = wl.make_append(pre, new, 2, 64, 16, "f16", seed=9, device=DEV)
+    check_case(case, "long runs of empty sequences")
+
+
 def test_append_then_decode_sees_the_new_tokens():
     """Append the last token of each sequence, then decode: equal to decoding
     a cache built with that token in place."""
