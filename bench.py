@@ -437,14 +437,14 @@ def bench_stream_copy_lib(pa, torch, steps, warmup, nbytes: int = 2 << 30, shape
     """The library's own read+write stream (pa_stream_copy: the non-temporal
     16-byte loads and stores of the block copy and the append) over a 2 GiB
     copy, for a few grid sizes; the fastest is the practical read+write
-    ceiling the copy and append kernels are set beside.  Shapes: one 16 KiB
+    ceiling the copy and append kernels are set beside.  Shapes: one 4 KiB
     chunk per work-group, and grid-stride loops over 32 or 128 work-groups
     per CU."""
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(3)
     dst = torch.empty_like(src)
     best = None
     sweep = {}
-    for wgs in shapes:                    # 0: one 16 KiB chunk per work-group
+    for wgs in shapes:                    # 0: one 4 KiB chunk per work-group
         timer = KernelTimer(pa, torch, steps)
         for _ in range(warmup):
             pa.pa_stream_copy(src, dst, wgs)
@@ -859,7 +859,7 @@ def main() -> int:
         extra["stream_read"] = r
         r = bench_stream_copy_lib(pa, torch, min(args.steps, 30), min(args.warmup, 10))
         log(f"  library copy stream: {r['GBps']:.0f} GB/s (read + write; shape {r['wgs_per_cu']}: "
-            f"0 = 16 KiB per work-group, else work-groups per CU)")
+            f"0 = 4 KiB per work-group, else work-groups per CU)")
         extra["stream_copy_lib"] = r
         for name in ("copy_bf16", "append_bf16"):
             extra[name]["frac_of_copy_stream"] = round(extra[name]["kernel_GBps"] / r["GBps"], 4)

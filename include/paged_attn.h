@@ -467,7 +467,7 @@ pa_status_t pa_stream_read(const void *src, int64_t bytes, uint32_t *sink, int32
  * Copies the `bytes` bytes at `src` to `dst` (device, both 16-byte aligned,
  * bytes a multiple of 16, else PA_ERR_UNSUPPORTED; overlapping ranges are
  * PA_ERR_SHAPE) with the non-temporal 16-byte loads and stores the block
- * copy and the KV append issue.  wgs_per_cu <= 0: one 16 KiB chunk per
+ * copy and the KV append issue.  wgs_per_cu <= 0: one 4 KiB chunk per
  * work-group (the fastest shape measured); > 0: a grid-stride loop over at
  * most wgs_per_cu work-groups per CU.  Its achieved GB/s (bytes read plus
  * bytes written) is the practical read+write ceiling those two kernels are

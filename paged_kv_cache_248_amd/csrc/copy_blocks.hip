@@ -11,7 +11,7 @@
 //   1. fill:    first_src[d] = INT32_MAX for every destination block;
 //   2. resolve: first_src[src_to_dst[i]] = min(i) with an atomic min, so the
 //               answer does not depend on execution order;
-//   3. copy:    one work-group per 16 KiB slice of a destination block of
+//   3. copy:    one work-group per 4 KiB slice of a destination block of
 //               one pool moves it with 16-byte non-temporal loads and stores
 //               (data is touched once; keeping it out of the caches leaves
 //               them to the attention kernels).
@@ -23,8 +23,8 @@ namespace pa {
 namespace {
 
 constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 4;
-constexpr int64_t kSliceBytes = (int64_t)kCopyThreads * 16 * kCopyUnroll;   // 16 KiB
+constexpr int kCopyUnroll = 1;
+constexpr int64_t kSliceBytes = (int64_t)kCopyThreads * 16 * kCopyUnroll;   // 4 KiB
 
 __global__ __launch_bounds__(256) void copy_fill_kernel(int32_t *first_src, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -42,11 +42,13 @@ __global__ __launch_bounds__(256) void copy_resolve_kernel(const int64_t *src_to
 __device__ __forceinline__ u32x4 ldnt(const u32x4 *p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void stnt(u32x4 *p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
-// One work-group per (pool, destination block, 16 KiB slice): it loads its
-// four 16-byte pieces per lane, then stores them.  A 2 GiB device copy of
-// this shape measured 6.1 TB/s on MI355X against 4.1 TB/s when one
-// work-group moved 32 KiB (eight pieces per lane), the shape of a
-// work-group that copies a slice of both pools.
+// One work-group per (pool, destination block, 4 KiB slice): each lane
+// loads one 16-byte piece, then stores it.  Smaller work-groups copied
+// faster on MI355X: on the 483 MB copy workload, slices of 4 / 8 / 16 KiB
+// (one, two, four pieces per lane) moved 5.94 / 5.63 / 5.70 TB/s, two
+// slices per work-group 5.18, and 1 / 2 / 8 KiB slices of one piece per
+// lane (64, 128, 512 threads) 5.92 / 5.87 / 5.85; an earlier 2 GiB copy
+// measured 4.1 TB/s at 32 KiB per work-group against 6.1 at 16 KiB.
 __global__ __launch_bounds__(256) void copy_kernel(const char *src_k, const char *src_v,
                                                    char *dst_k, char *dst_v,
                                                    const int32_t *first_src, int64_t num_src,

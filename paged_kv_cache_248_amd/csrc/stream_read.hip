@@ -45,24 +45,26 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const u32x4
 
 // Copy stream: every 16-byte piece is loaded and stored once with
 // non-temporal accesses (the kind the block copy and the append issue).
-// Default shape: one 16 KiB chunk per work-group, each lane loading its four
-// pieces and then storing them (the fastest of the shapes measured on
-// MI355X: 6.1 TB/s of reads plus writes for 2 GiB, against 4.1-5.2 TB/s for
-// 32 KiB or 64 KiB chunks and for grid-stride loops); the grid-stride form
-// stays available for comparison.
-constexpr int kCopyUnroll = 4;
+// Default shape: one 4 KiB chunk per work-group, each lane loading one
+// piece and then storing it (the fastest of the shapes measured on MI355X:
+// 6.41-6.44 TB/s of reads plus writes for 2 GiB against 6.18-6.25 for
+// 16 KiB chunks of four pieces per lane, 4.1 for 32 KiB or 64 KiB chunks and
+// 5.1-5.2 for grid-stride loops of four pieces per lane, which stay
+// available for comparison).
+constexpr int kCopyChunkPieces = 1;   // pieces per lane, chunked form
+constexpr int kCopyUnroll = 4;        // pieces per lane and step, grid-stride form
 
 __global__ __launch_bounds__(kStreamThreads) void stream_copy_chunk_kernel(
     const u32x4 *__restrict__ src, u32x4 *__restrict__ dst, int64_t n16) {
-  const int64_t base = (int64_t)blockIdx.x * kStreamThreads * kCopyUnroll + threadIdx.x;
-  u32x4 v[kCopyUnroll];
+  const int64_t base = (int64_t)blockIdx.x * kStreamThreads * kCopyChunkPieces + threadIdx.x;
+  u32x4 v[kCopyChunkPieces];
 #pragma unroll
-  for (int u = 0; u < kCopyUnroll; ++u) {
+  for (int u = 0; u < kCopyChunkPieces; ++u) {
     const int64_t i = base + (int64_t)u * kStreamThreads;
     if (i < n16) v[u] = __builtin_nontemporal_load(src + i);
   }
 #pragma unroll
-  for (int u = 0; u < kCopyUnroll; ++u) {
+  for (int u = 0; u < kCopyChunkPieces; ++u) {
     const int64_t i = base + (int64_t)u * kStreamThreads;
     if (i < n16) __builtin_nontemporal_store(v[u], dst + i);
   }
@@ -141,7 +143,8 @@ hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes, int32_t
   const int64_t per_wg = (int64_t)kStreamThreads * kCopyUnroll;
   profile_begin(stream);
   if (wgs_per_cu <= 0) {
-    const int64_t grid = (n16 + per_wg - 1) / per_wg;
+    const int64_t per_chunk = (int64_t)kStreamThreads * kCopyChunkPieces;
+    const int64_t grid = (n16 + per_chunk - 1) / per_chunk;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(stream_copy_chunk_kernel, dim3((unsigned)grid), dim3(kStreamThreads), 0,
                        stream, static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), n16);
