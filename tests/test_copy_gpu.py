@@ -66,10 +66,11 @@ def test_nan_payloads_and_negative_zero_survive():
     assert torch.equal(dst.view(torch.int16).cpu(), src.flip(0).view(torch.int16).cpu())
 
 
-def test_large_block_spans_several_slices():
-    # 48 KiB blocks: three 16 KiB slices per block
-    src = torch.randn(6, 3, 64, 64, device=DEV)
-    dst = torch.zeros(5, 3, 64, 64, device=DEV)
+@pytest.mark.parametrize("shape,dt", [((3, 64, 64), torch.float32),    # 48 KiB: 12 whole 4 KiB slices
+                                      ((5, 16, 64), torch.float16)])   # 10 KiB: the third slice half full
+def test_large_block_spans_several_slices(shape, dt):
+    src = torch.randn(6, *shape, device=DEV).to(dt)
+    dst = torch.zeros(5, *shape, device=DEV).to(dt)
     m = torch.tensor([4, 0, -1, 2, 0, 1], dtype=torch.int64, device=DEV)
     want = copy_blocks_ref(bits(src).reshape(6, -1), bits(dst).reshape(5, -1), m.cpu().numpy())
     pa.paged_kv_copy_blocks(src, None, dst, None, m)
