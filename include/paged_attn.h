@@ -305,7 +305,10 @@ pa_status_t paged_attn_prefill_unfused(void *out, const void *query, const void 
  *                 16-byte aligned (else PA_ERR_WORKSPACE)
  *
  * Source and destination pools must not overlap.  num_mappings may be 0
- * (nothing is launched) and must be below 2^31.
+ * (nothing is launched) and must be below 2^31.  The copy runs one
+ * work-group per 4 KiB slice of each destination block of each pool, so
+ * num_dst_blocks * ceil(block_bytes / 4096) must not exceed 2^30 - 1
+ * (else PA_ERR_SHAPE).
  * ------------------------------------------------------------------------ */
 size_t paged_kv_copy_blocks_workspace_size(int64_t num_dst_blocks);
 

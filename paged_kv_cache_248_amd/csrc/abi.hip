@@ -482,7 +482,7 @@ pa_status_t paged_kv_copy_blocks(const void *src_k, const void *src_v, void *dst
       num_dst_blocks < 0 || block_bytes <= 0)
     return PA_ERR_SHAPE;
   if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
-  const int64_t slices = (block_bytes + 16383) / 16384;
+  const int64_t slices = (block_bytes + pa::kCopySliceBytes - 1) / pa::kCopySliceBytes;
   // one work-group per (pool, destination block, slice)
   if (num_dst_blocks > 0 && slices > (int64_t)(INT32_MAX / 2) / num_dst_blocks) return PA_ERR_SHAPE;
   if (num_mappings == 0 || num_dst_blocks == 0 || num_src_blocks == 0) return PA_OK;

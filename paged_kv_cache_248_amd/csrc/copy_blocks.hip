@@ -25,6 +25,7 @@ namespace {
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 1;
 constexpr int64_t kSliceBytes = (int64_t)kCopyThreads * 16 * kCopyUnroll;   // 4 KiB
+static_assert(kSliceBytes == kCopySliceBytes, "the argument checks size the grid by this slice");
 
 __global__ __launch_bounds__(256) void copy_fill_kernel(int32_t *first_src, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;

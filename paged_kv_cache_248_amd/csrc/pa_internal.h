@@ -59,6 +59,11 @@ hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t stream);
 // The same prefill with the half-tile schedule (prefill_halftile.hip).
 hipError_t launch_prefill_halftile(const PrefillLaunch &a, hipStream_t stream);
 
+// Bytes of a destination block one copy work-group moves (one 16-byte piece
+// per lane of 256); the grid is one work-group per (pool, destination block,
+// slice), so the argument checks bound it with the same figure.
+constexpr int64_t kCopySliceBytes = 4096;
+
 struct CopyLaunch {
   const void *src_k, *src_v;
   void *dst_k, *dst_v;
@@ -117,7 +122,7 @@ pa_gemm_status launch_prefill_unfused(const UnfusedLaunch &a, hipStream_t stream
 hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, int32_t sink_words,
                               hipStream_t stream);
 
-// Copies `bytes` (a multiple of 16) from src to dst once: one 16 KiB chunk
+// Copies `bytes` (a multiple of 16) from src to dst once: one 4 KiB chunk
 // per work-group (wgs_per_cu <= 0), or a grid-stride loop over at most
 // wgs_per_cu work-groups per CU.
 hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes, int32_t wgs_per_cu,

@@ -180,6 +180,9 @@ def _copy(lib, **kw):
     (dict(nm=-1), PA_ERR_SHAPE),
     (dict(nm=1 << 31), PA_ERR_SHAPE),
     (dict(bb=24), PA_ERR_UNSUPPORTED),
+    # one work-group per (pool, destination block, 4 KiB slice) must fit the grid
+    (dict(bb=16384, nd=1 << 28), PA_ERR_SHAPE),
+    (dict(bb=4096, nd=1 << 30), PA_ERR_SHAPE),
     (dict(sk=None), PA_ERR_NULL),
     (dict(m=None), PA_ERR_NULL),
     (dict(sv=None), PA_ERR_NULL),           # V pair half given
