@@ -53,18 +53,17 @@ __device__ __forceinline__ void stnt(u32x4 *p, u32x4 v) { __builtin_nontemporal_
 __global__ __launch_bounds__(256) void copy_kernel(const char *src_k, const char *src_v,
                                                    char *dst_k, char *dst_v,
                                                    const int32_t *first_src, int64_t num_src,
-                                                   int64_t block_bytes, int64_t slices,
-                                                   int64_t num_dst) {
-  const int64_t item = blockIdx.x;
-  const int64_t pool = item / (num_dst * slices);            // 0: K, 1: V
-  const int64_t rest = item - pool * num_dst * slices;
-  const int64_t d = rest / slices;
-  const int64_t slice = rest - d * slices;
+                                                   int64_t block_bytes, uint32_t slices) {
+  // blockIdx.x = destination block * slices + slice (below 2^31, checked by
+  // the caller), blockIdx.y = pool (0: K, 1: V): one 32-bit division.
+  const uint32_t x = blockIdx.x;
+  const uint32_t d = x / slices;
+  const uint32_t slice = x - d * slices;
   const int32_t i = first_src[d];
   if ((int64_t)i >= num_src) return;    // no valid source (INT32_MAX if nobody named d)
-  const char *src = pool == 0 ? src_k : src_v;
-  char *dst = pool == 0 ? dst_k : dst_v;
-  const int64_t base = slice * kSliceBytes;
+  const char *src = blockIdx.y == 0 ? src_k : src_v;
+  char *dst = blockIdx.y == 0 ? dst_k : dst_v;
+  const int64_t base = (int64_t)slice * kSliceBytes;
   const size_t so = (size_t)i * block_bytes, dof = (size_t)d * block_bytes;
   u32x4 r[kCopyUnroll];
 #pragma unroll
@@ -90,12 +89,12 @@ hipError_t launch_copy_blocks(const CopyLaunch &a, hipStream_t stream) {
   hipLaunchKernelGGL(copy_resolve_kernel, dim3((unsigned)res_blocks), dim3(256), 0, stream,
                      a.src_to_dst, a.num_mappings, a.num_dst, a.first_src);
   const int64_t slices = (a.block_bytes + kSliceBytes - 1) / kSliceBytes;
-  const int64_t grid = slices * a.num_dst * (a.src_v ? 2 : 1);
+  const int64_t grid = slices * a.num_dst;            // below 2^31 (argument checks)
   profile_begin(stream);
-  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)grid), dim3(kCopyThreads), 0, stream,
-                     static_cast<const char *>(a.src_k), static_cast<const char *>(a.src_v),
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)grid, a.src_v ? 2 : 1), dim3(kCopyThreads), 0,
+                     stream, static_cast<const char *>(a.src_k), static_cast<const char *>(a.src_v),
                      static_cast<char *>(a.dst_k), static_cast<char *>(a.dst_v), a.first_src,
-                     a.num_src, a.block_bytes, slices, a.num_dst);
+                     a.num_src, a.block_bytes, (uint32_t)slices);
   profile_end(stream);
   return hipGetLastError();
 }
