@@ -50,7 +50,8 @@ def log(msg: str) -> None:
 
 
 class KernelTimer:
-    """HIP events recorded by the library around its main kernel."""
+    """HIP events that the library has the runtime record as part of its main
+    kernel's dispatch (start and end of that kernel's execution)."""
 
     def __init__(self, pa, torch, n: int):
         self.pa, self.torch = pa, torch

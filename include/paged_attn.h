@@ -436,11 +436,14 @@ pa_status_t pa_bm_fill_batch(const pa_block_manager *bm, const int64_t *request_
 /* --------------------------------------------------------------------------
  * Measurement hook.
  *
- * With non-NULL events (hipEvent_t passed as void*, created by the caller),
- * every later call records `start` on its stream just before its main kernel
- * (decode: the attention kernel; prefill: the attention kernel; copy: the copy
- * kernel; append: the append kernel) and `stop` just after it, so the caller
- * can read that kernel's duration with hipEventElapsedTime.  Pass NULL, NULL to stop recording.  The
+ * With non-NULL events (hipEvent_t passed as void*, created by the caller
+ * with timing enabled), every later call has the runtime record `start` and
+ * `stop` as part of its main kernel's dispatch (decode: the attention
+ * kernel; prefill: the attention kernel; copy: the copy kernel; append: the
+ * append kernel): the two events bracket that kernel's execution, the span a
+ * kernel trace reports, and add no packets of their own to the stream, so
+ * the caller can read the kernel's duration with hipEventElapsedTime.  Pass
+ * NULL, NULL to stop recording (calls then launch plainly).  The
  * setting is process-wide and not synchronised: set it from the thread that
  * issues the calls being measured.  Returns PA_ERR_NULL if exactly one event
  * is NULL.

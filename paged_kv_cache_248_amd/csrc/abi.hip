@@ -34,12 +34,8 @@ hipEvent_t g_prof_start = nullptr;
 hipEvent_t g_prof_stop = nullptr;
 }  // namespace
 
-void profile_begin(hipStream_t stream) {
-  if (g_prof_start) (void)hipEventRecord(g_prof_start, stream);
-}
-void profile_end(hipStream_t stream) {
-  if (g_prof_stop) (void)hipEventRecord(g_prof_stop, stream);
-}
+hipEvent_t profile_start_event() { return g_prof_start; }
+hipEvent_t profile_stop_event() { return g_prof_stop; }
 
 }  // namespace pa
 

@@ -156,10 +156,7 @@ hipError_t launch_append(const AppendLaunch &a, hipStream_t stream) {
   p.pieces = a.num_kv_heads * p.head_bytes / 16;
   p.tensors = a.v_cache ? 2 : 1;
   const int grid = (a.total_tokens + kTokensPerGroup - 1) / kTokensPerGroup;
-  profile_begin(stream);
-  hipLaunchKernelGGL(append_kernel, dim3(grid), dim3(256), 0, stream, p);
-  profile_end(stream);
-  return hipGetLastError();
+  return launch_main(append_kernel, dim3(grid), dim3(256), 0, stream, p);
 }
 
 }  // namespace pa

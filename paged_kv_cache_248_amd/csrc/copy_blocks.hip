@@ -90,13 +90,11 @@ hipError_t launch_copy_blocks(const CopyLaunch &a, hipStream_t stream) {
                      a.src_to_dst, a.num_mappings, a.num_dst, a.first_src);
   const int64_t slices = (a.block_bytes + kSliceBytes - 1) / kSliceBytes;
   const int64_t grid = slices * a.num_dst;            // below 2^31 (argument checks)
-  profile_begin(stream);
-  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)grid, a.src_v ? 2 : 1), dim3(kCopyThreads), 0,
+  return launch_main(copy_kernel, dim3((unsigned)grid, a.src_v ? 2 : 1), dim3(kCopyThreads), 0,
                      stream, static_cast<const char *>(a.src_k), static_cast<const char *>(a.src_v),
-                     static_cast<char *>(a.dst_k), static_cast<char *>(a.dst_v), a.first_src,
-                     a.num_src, a.block_bytes, (uint32_t)slices);
-  profile_end(stream);
-  return hipGetLastError();
+                     static_cast<char *>(a.dst_k), static_cast<char *>(a.dst_v),
+                     static_cast<const int32_t *>(a.first_src), a.num_src, a.block_bytes,
+                     (uint32_t)slices);
 }
 
 }  // namespace pa

@@ -978,10 +978,7 @@ hipError_t launch_typed(const DecodeLaunch &a, const DecodeWorkspace &ws, hipStr
   const long long resident = (long long)device_cu_count() * occ;
   const int grid = p.direct ? (int)std::max(1LL, upper)
                             : (int)std::max(1LL, std::min(upper, resident));
-  profile_begin(stream);
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, stream, p);
-  profile_end(stream);
-  return hipGetLastError();
+  return launch_main(kernel, dim3(grid), dim3(256), 0, stream, p);
 }
 
 template <class E, int D>

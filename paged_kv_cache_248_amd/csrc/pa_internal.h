@@ -1,6 +1,7 @@
 // Internal launcher interface between the C ABI layer and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -138,8 +139,23 @@ hipError_t launch_mfma_stream(const void *ops, int64_t ops_bytes, float *sink, i
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
-// Records the caller's measurement events (if set) around a main kernel.
-void profile_begin(hipStream_t stream);
-void profile_end(hipStream_t stream);
+// The caller's measurement events (pa_set_profile_events), or nullptr.
+hipEvent_t profile_start_event();
+hipEvent_t profile_stop_event();
+
+// Launches a main kernel.  With measurement events set, the runtime records
+// them as part of the kernel's own dispatch (start and end of its
+// execution, the span a kernel trace reports), with no separate event
+// packets in the stream; without them it is a plain launch.
+template <class F, class... Args>
+hipError_t launch_main(F kernel, dim3 grid, dim3 block, uint32_t lds_bytes, hipStream_t stream,
+                       Args... args) {
+  hipEvent_t start = profile_start_event(), stop = profile_stop_event();
+  if (start && stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, start, stop, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, args...);
+  return hipGetLastError();
+}
 
 }  // namespace pa

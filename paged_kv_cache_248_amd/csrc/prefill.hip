@@ -468,11 +468,8 @@ hipError_t launch_typed(const PrefillLaunch &a, hipStream_t stream) {
   e = prefill_allow_lds(reinterpret_cast<const void *>(&prefill_kernel<E, D>), lds_bytes, dev,
                         attr_devices);
   if (e != hipSuccess) return e;
-  profile_begin(stream);
-  hipLaunchKernelGGL((prefill_kernel<E, D>), dim3((unsigned)grid), dim3(64 * kWaves), lds_bytes,
-                     stream, p);
-  profile_end(stream);
-  return hipGetLastError();
+  return launch_main(prefill_kernel<E, D>, dim3((unsigned)grid), dim3(64 * kWaves),
+                     (uint32_t)lds_bytes, stream, p);
 }
 
 }  // namespace

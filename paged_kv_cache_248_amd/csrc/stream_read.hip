@@ -141,22 +141,18 @@ hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes, int32_t
                               hipStream_t stream) {
   const int64_t n16 = bytes / 16;
   const int64_t per_wg = (int64_t)kStreamThreads * kCopyUnroll;
-  profile_begin(stream);
   if (wgs_per_cu <= 0) {
     const int64_t per_chunk = (int64_t)kStreamThreads * kCopyChunkPieces;
     const int64_t grid = (n16 + per_chunk - 1) / per_chunk;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(stream_copy_chunk_kernel, dim3((unsigned)grid), dim3(kStreamThreads), 0,
+    return launch_main(stream_copy_chunk_kernel, dim3((unsigned)grid), dim3(kStreamThreads), 0,
                        stream, static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), n16);
-  } else {
-    const int64_t want = (n16 + per_wg - 1) / per_wg;
-    const int64_t cap = (int64_t)device_cu_count() * wgs_per_cu;
-    const int grid = (int)(want < 1 ? 1 : (want < cap ? want : cap));
-    hipLaunchKernelGGL(stream_copy_kernel, dim3(grid), dim3(kStreamThreads), 0, stream,
-                       static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), n16);
   }
-  profile_end(stream);
-  return hipGetLastError();
+  const int64_t want = (n16 + per_wg - 1) / per_wg;
+  const int64_t cap = (int64_t)device_cu_count() * wgs_per_cu;
+  const int grid = (int)(want < 1 ? 1 : (want < cap ? want : cap));
+  return launch_main(stream_copy_kernel, dim3(grid), dim3(kStreamThreads), 0, stream,
+                     static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), n16);
 }
 
 hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, int32_t sink_words,
@@ -167,11 +163,8 @@ hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, in
   int64_t cap = (int64_t)device_cu_count() * 128;
   if (cap > sink_words) cap = sink_words;
   const int grid = (int)(want < 1 ? 1 : (want < cap ? want : cap));
-  profile_begin(stream);
-  hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(kStreamThreads), 0, stream,
+  return launch_main(stream_read_kernel, dim3(grid), dim3(kStreamThreads), 0, stream,
                      static_cast<const u32x4 *>(src), n16, sink);
-  profile_end(stream);
-  return hipGetLastError();
 }
 
 hipError_t launch_mfma_stream(const void *ops, int64_t ops_bytes, float *sink, int32_t sink_words,
@@ -179,15 +172,11 @@ hipError_t launch_mfma_stream(const void *ops, int64_t ops_bytes, float *sink, i
   const int64_t want = (int64_t)device_cu_count() * wgs_per_cu;
   const int grid = (int)(want < sink_words ? want : sink_words);
   const int64_t n16 = ops_bytes / 16;
-  profile_begin(stream);
   if (dtype == DType::F16)
-    hipLaunchKernelGGL(mfma_stream_kernel<F16>, dim3(grid), dim3(kStreamThreads), 0, stream,
+    return launch_main(mfma_stream_kernel<F16>, dim3(grid), dim3(kStreamThreads), 0, stream,
                        static_cast<const u32x4 *>(ops), n16, sink, iters);
-  else
-    hipLaunchKernelGGL(mfma_stream_kernel<BF16>, dim3(grid), dim3(kStreamThreads), 0, stream,
-                       static_cast<const u32x4 *>(ops), n16, sink, iters);
-  profile_end(stream);
-  return hipGetLastError();
+  return launch_main(mfma_stream_kernel<BF16>, dim3(grid), dim3(kStreamThreads), 0, stream,
+                     static_cast<const u32x4 *>(ops), n16, sink, iters);
 }
 
 }  // namespace pa
