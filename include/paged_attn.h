@@ -443,7 +443,8 @@ pa_status_t pa_bm_fill_batch(const pa_block_manager *bm, const int64_t *request_
  * append kernel): the two events bracket that kernel's execution, the span a
  * kernel trace reports, and add no packets of their own to the stream, so
  * the caller can read the kernel's duration with hipEventElapsedTime.  Pass
- * NULL, NULL to stop recording (calls then launch plainly).  The
+ * NULL, NULL to stop recording (calls then launch plainly); leave them
+ * unset while capturing a HIP graph, whose launches must be plain.  The
  * setting is process-wide and not synchronised: set it from the thread that
  * issues the calls being measured.  Returns PA_ERR_NULL if exactly one event
  * is NULL.
